@@ -1,0 +1,216 @@
+"""ctypes binding of libcbq.so.
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+torch supplies device memory (output tensors are allocated here with torch) and the
+current HIP stream.  There is no CPU or Python fallback: if the library is missing or
+the GPU is absent, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libcbq.so")
+
+CBQ_OK, CBQ_EINVAL, CBQ_EUNSUPPORTED, CBQ_EWORKSPACE, CBQ_EHIP = 0, -1, -2, -3, -4
+EPI_F32, EPI_SWIGLU_BF16 = 0, 1
+PATH_AUTO, PATH_LUT, PATH_MFMA = 0, 1, 2
+AUTO_MAX_LUT_ROWS = 32
+
+# every symbol include/cbq.h declares
+EXPORTED = ("cbq_rotate_quantize", "cbq_route_workspace", "cbq_moe_route_gather",
+            "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
+            "cbq_status_string", "cbq_last_error", "cbq_version")
+
+
+class CbqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class cbq_weights(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("codebook", ctypes.c_void_p), ("E", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libcbq.so (built in-tree by codebook_bit_quantized_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libcbq.so not found at {path}; build it with "
+                          "`python -m codebook_bit_quantized_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    W = ctypes.POINTER(cbq_weights)
+    sig = {
+        "cbq_rotate_quantize": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
+        "cbq_route_workspace": (sz, [i64, i32, i32, i32]),
+        "cbq_moe_route_gather": (ctypes.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                vp, sz, vp]),
+        "cbq_gemm_workspace": (sz, [W, i32, i64, i32, i32]),
+        "cbq_codebook_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, vp, vp, W, i32, i32, i32, vp,
+                                                 i64, vp, sz, vp]),
+        "cbq_moe_combine": (ctypes.c_int, [vp, vp, vp, i64, i32, i32, i32, vp, vp]),
+        "cbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "cbq_last_error": (ctypes.c_char_p, []),
+        "cbq_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != CBQ_OK:
+        lib = load_library()
+        raise CbqError(status, f"{lib.cbq_status_string(status).decode()}: "
+                               f"{lib.cbq_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _require_gpu(*ts: Optional[torch.Tensor]):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("cbq operates on device tensors only")
+
+
+@dataclass
+class CodebookWeights:
+    """One weight matrix type for E experts: packed indices and fp16 codebooks (device)."""
+    idx: torch.Tensor        # uint8 [E][N][K*bits/8]
+    codebook: torch.Tensor   # int16/uint16/float16 [E][N][2^bits]
+    K: int
+    bits: int
+
+    @property
+    def E(self) -> int:
+        return self.idx.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.idx.shape[1]
+
+    def c_struct(self) -> cbq_weights:
+        return cbq_weights(self.idx.data_ptr(), self.codebook.data_ptr(), self.E, self.N, self.K,
+                           self.bits)
+
+
+# ---------------------------------------------------------------------------
+def rotate_quantize(x: torch.Tensor, act_bits: int = 4, had_block: int = 0,
+                    codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                    precond: Optional[torch.Tensor] = None, stream=None):
+    """x: bf16 (or int16 bit patterns) [T][K] on the GPU -> (codes uint8, scales fp32)."""
+    lib = load_library()
+    _require_gpu(x)
+    T, K = x.shape
+    ldx = x.stride(0)
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along channels")
+    if codes is None:
+        codes = torch.empty((T, K * act_bits // 8), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _check(lib.cbq_rotate_quantize(_ptr(x), T, K, ldx, had_block, act_bits, _ptr(codes),
+                                   _ptr(scales), _ptr(precond), _stream(stream)))
+    return codes, scales
+
+
+def moe_route_gather(logits: torch.Tensor, topk: int, renormalize: bool = True, n_shared: int = 0,
+                     out: Optional[dict] = None, stream=None) -> dict:
+    """logits fp32 [T][E] -> dict(ids, weights, offsets, sorted_tokens, slot_of)."""
+    lib = load_library()
+    _require_gpu(logits)
+    T, E = logits.shape
+    dev = logits.device
+    o = out or {}
+    ids = o.get("ids") if o.get("ids") is not None else torch.empty((T, topk), dtype=torch.int32, device=dev)
+    w = o.get("weights") if o.get("weights") is not None else torch.empty((T, topk), dtype=torch.float32, device=dev)
+    offs = o.get("offsets") if o.get("offsets") is not None else torch.empty((E + n_shared + 1,), dtype=torch.int32, device=dev)
+    R = T * topk + n_shared * T
+    st = o.get("sorted_tokens") if o.get("sorted_tokens") is not None else torch.empty((max(R, 1),), dtype=torch.int32, device=dev)
+    so = o.get("slot_of") if o.get("slot_of") is not None else torch.empty((T, topk), dtype=torch.int32, device=dev)
+    _check(lib.cbq_moe_route_gather(_ptr(logits), T, E, topk, int(bool(renormalize)), n_shared,
+                                    _ptr(ids), _ptr(w), _ptr(offs), _ptr(st), _ptr(so), None, 0,
+                                    _stream(stream)))
+    return dict(ids=ids, weights=w, offsets=offs, sorted_tokens=st[:R], slot_of=so)
+
+
+def codebook_lut_gemm(codes: torch.Tensor, scales: torch.Tensor, act_bits: int,
+                      weights: Sequence[CodebookWeights], n_rows: Optional[int] = None,
+                      expert_offsets: Optional[torch.Tensor] = None,
+                      row_token: Optional[torch.Tensor] = None, epilogue: Optional[int] = None,
+                      path: int = PATH_AUTO, out: Optional[torch.Tensor] = None, stream=None):
+    """Grouped codebook GEMM.  One weight set -> fp32 [R][N]; {gate, up} -> bf16 SwiGLU [R][N]."""
+    lib = load_library()
+    _require_gpu(codes, scales, expert_offsets, row_token)
+    n_w = len(weights)
+    if epilogue is None:
+        epilogue = EPI_SWIGLU_BF16 if n_w == 2 else EPI_F32
+    if n_rows is None:
+        n_rows = row_token.shape[0] if row_token is not None else codes.shape[0]
+    N = weights[0].N
+    if out is None:
+        dt = torch.bfloat16 if epilogue == EPI_SWIGLU_BF16 else torch.float32
+        out = torch.empty((n_rows, N), dtype=dt, device=codes.device)
+    arr = (cbq_weights * n_w)(*[w.c_struct() for w in weights])
+    _check(lib.cbq_codebook_lut_gemm(_ptr(codes), _ptr(scales), act_bits, n_rows,
+                                     _ptr(expert_offsets), _ptr(row_token), arr, n_w, epilogue,
+                                     path, _ptr(out), out.stride(0), None, 0, _stream(stream)))
+    return out
+
+
+def moe_combine(expert_out: torch.Tensor, slot_of: torch.Tensor, topk_w: torch.Tensor,
+                n_shared: int = 0, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    lib = load_library()
+    _require_gpu(expert_out, slot_of, topk_w)
+    T, topk = slot_of.shape
+    H = expert_out.shape[1]
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=expert_out.device)
+    _check(lib.cbq_moe_combine(_ptr(expert_out), _ptr(slot_of), _ptr(topk_w), T, topk, H, n_shared,
+                               _ptr(y), _stream(stream)))
+    return y
+
+
+def moe_ffn(x: torch.Tensor, logits: torch.Tensor, gate: CodebookWeights, up: CodebookWeights,
+            down: CodebookWeights, topk: int, n_shared: int = 0, act_bits: int = 4,
+            renormalize: bool = True, path: int = PATH_AUTO, keep: bool = False, stream=None):
+    """One MoE FFN layer as a sequence of the four library calls (no compute here).
+
+    gate/up/down hold E routed + n_shared shared experts.  Returns y fp32 [T][H], or
+    (y, intermediates) when keep is True."""
+    codes, scales = rotate_quantize(x, act_bits, stream=stream)
+    rt = moe_route_gather(logits, topk, renormalize, n_shared, stream=stream)
+    h = codebook_lut_gemm(codes, scales, act_bits, [gate, up], expert_offsets=rt["offsets"],
+                          row_token=rt["sorted_tokens"], path=path, stream=stream)
+    codes_h, scales_h = rotate_quantize(h, act_bits, stream=stream)
+    out = codebook_lut_gemm(codes_h, scales_h, act_bits, [down], expert_offsets=rt["offsets"],
+                            path=path, stream=stream)
+    y = moe_combine(out, rt["slot_of"], rt["weights"], n_shared, stream=stream)
+    if keep:
+        return y, dict(codes=codes, scales=scales, route=rt, h=h, codes_h=codes_h,
+                       scales_h=scales_h, out=out)
+    return y

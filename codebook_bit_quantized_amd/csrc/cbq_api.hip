@@ -1,0 +1,183 @@
+// C ABI of libcbq: argument validation (host only, before any HIP call), dispatch to
+// the kernels, status codes and the per-thread error message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/cbq.h"
+#include "cbq_internal.hpp"
+
+#define CBQ_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(CBQ_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_weights(const cbq_weights* W, int i) {
+  if (!W->idx || !W->codebook) return fail(CBQ_EINVAL, "W[%d]: idx and codebook must be non-null", i);
+  if (!aligned16(W->idx) || !aligned16(W->codebook))
+    return fail(CBQ_EINVAL, "W[%d]: idx and codebook must be 16-byte aligned", i);
+  if (W->E < 1) return fail(CBQ_EINVAL, "W[%d]: E must be >= 1 (got %d)", i, W->E);
+  if (W->N < 16 || W->N % 16) return fail(CBQ_EINVAL, "W[%d]: N must be a positive multiple of 16 (got %d)", i, W->N);
+  if (W->K < 32 || W->K % 32) return fail(CBQ_EINVAL, "W[%d]: K must be a positive multiple of 32 (got %d)", i, W->K);
+  if (W->bits < 2 || W->bits > 4) return fail(CBQ_EUNSUPPORTED, "W[%d]: bits must be 2, 3 or 4 (got %d)", i, W->bits);
+  return CBQ_OK;
+}
+
+}  // namespace
+
+CBQ_EXPORT const char* cbq_status_string(int status) {
+  switch (status) {
+    case CBQ_OK: return "CBQ_OK";
+    case CBQ_EINVAL: return "CBQ_EINVAL";
+    case CBQ_EUNSUPPORTED: return "CBQ_EUNSUPPORTED";
+    case CBQ_EWORKSPACE: return "CBQ_EWORKSPACE";
+    case CBQ_EHIP: return "CBQ_EHIP";
+  }
+  return "CBQ_UNKNOWN";
+}
+
+CBQ_EXPORT const char* cbq_last_error(void) { return g_err; }
+
+CBQ_EXPORT int cbq_version(void) { return 100; }
+
+CBQ_EXPORT int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
+                                   int32_t had_block, int32_t act_bits, uint8_t* codes,
+                                   float* scales, uint32_t* precond_violations, void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
+  if (T > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "T must be < 2^31");
+  if (K < 32 || K % 32) return fail(CBQ_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (K > 16384) return fail(CBQ_EUNSUPPORTED, "K must be <= 16384 (got %d)", K);
+  if (ldx < K || ldx % 8) return fail(CBQ_EINVAL, "ldx must be >= K and a multiple of 8 (got %lld)", (long long)ldx);
+  if (act_bits != 4 && act_bits != 8) return fail(CBQ_EINVAL, "act_bits must be 4 or 8 (got %d)", act_bits);
+  int b = had_block;
+  if (b == 0) b = K & -K;
+  if (!pow2(b) || K % b) return fail(CBQ_EINVAL, "had_block must be 0 or a power of two dividing K (got %d)", had_block);
+  if (T == 0) return CBQ_OK;
+  if (!x || !codes || !scales) return fail(CBQ_EINVAL, "x, codes and scales must be non-null");
+  if (!aligned16(x) || !aligned16(codes)) return fail(CBQ_EINVAL, "x and codes must be 16-byte aligned");
+  hipError_t e = cbq::launch_rotate_quantize(x, T, K, ldx, b, act_bits, codes, scales,
+                                             precond_violations, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rotate_quantize launch");
+  return CBQ_OK;
+}
+
+CBQ_EXPORT size_t cbq_route_workspace(int64_t T, int32_t E, int32_t topk, int32_t n_shared) {
+  (void)T; (void)E; (void)topk; (void)n_shared;
+  return 0;
+}
+
+CBQ_EXPORT int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk,
+                                    int32_t renormalize, int32_t n_shared, int32_t* topk_ids,
+                                    float* topk_w, int32_t* expert_offsets,
+                                    int32_t* sorted_tokens, int32_t* slot_of, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)ws; (void)ws_bytes;
+  if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
+  if (T > (1 << 24)) return fail(CBQ_EUNSUPPORTED, "T must be <= 2^24");
+  if (E < 1 || E > 256) return fail(CBQ_EUNSUPPORTED, "E must be in [1, 256] (got %d)", E);
+  if (topk < 1 || topk > 8 || topk > E) return fail(CBQ_EINVAL, "topk must be in [1, min(E, 8)] (got %d)", topk);
+  if (n_shared < 0 || n_shared > 8) return fail(CBQ_EINVAL, "n_shared must be in [0, 8] (got %d)", n_shared);
+  if (renormalize != 0 && renormalize != 1) return fail(CBQ_EINVAL, "renormalize must be 0 or 1");
+  if (!expert_offsets) return fail(CBQ_EINVAL, "expert_offsets must be non-null");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_tokens || !slot_of))
+    return fail(CBQ_EINVAL, "logits, topk_ids, topk_w, sorted_tokens and slot_of must be non-null");
+  hipError_t e = cbq::launch_route(logits, T, E, topk, renormalize, n_shared, topk_ids, topk_w,
+                                   expert_offsets, sorted_tokens, slot_of, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_gather launch");
+  return CBQ_OK;
+}
+
+CBQ_EXPORT size_t cbq_gemm_workspace(const cbq_weights* W, int32_t n_w, int64_t n_rows,
+                                     int32_t act_bits, int32_t path) {
+  (void)W; (void)n_w; (void)n_rows; (void)act_bits; (void)path;
+  return 0;
+}
+
+CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits,
+                                     int64_t n_rows, const int32_t* expert_offsets,
+                                     const int32_t* row_token, const cbq_weights* W, int32_t n_w,
+                                     int32_t epilogue, int32_t path, void* out, int64_t ldo,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)ws; (void)ws_bytes;
+  if (!W) return fail(CBQ_EINVAL, "W must be non-null");
+  if (n_w != 1 && n_w != 2) return fail(CBQ_EINVAL, "n_w must be 1 or 2 (got %d)", n_w);
+  for (int i = 0; i < n_w; ++i) {
+    int st = check_weights(&W[i], i);
+    if (st != CBQ_OK) return st;
+  }
+  if (n_w == 2 && (W[1].E != W[0].E || W[1].N != W[0].N || W[1].K != W[0].K || W[1].bits != W[0].bits))
+    return fail(CBQ_EINVAL, "gate and up weights must have equal E, N, K and bits");
+  if (act_bits != 4 && act_bits != 8) return fail(CBQ_EINVAL, "act_bits must be 4 or 8 (got %d)", act_bits);
+  if (epilogue == CBQ_EPI_F32) {
+    if (n_w != 1) return fail(CBQ_EINVAL, "CBQ_EPI_F32 takes exactly one weight set");
+  } else if (epilogue == CBQ_EPI_SWIGLU_BF16) {
+    if (n_w != 2) return fail(CBQ_EINVAL, "CBQ_EPI_SWIGLU_BF16 takes the gate and up weight sets (n_w = 2)");
+  } else {
+    return fail(CBQ_EINVAL, "unknown epilogue %d", epilogue);
+  }
+  if (path < CBQ_PATH_AUTO || path > CBQ_PATH_MFMA) return fail(CBQ_EINVAL, "unknown path %d", path);
+  if (n_rows < 0) return fail(CBQ_EINVAL, "n_rows must be >= 0");
+  if (n_rows > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "n_rows must be < 2^31");
+  if (ldo < W[0].N || ldo % 4) return fail(CBQ_EINVAL, "ldo must be >= N and a multiple of 4 (got %lld)", (long long)ldo);
+  if (n_rows == 0) return CBQ_OK;
+  if (!codes || !scales || !out) return fail(CBQ_EINVAL, "codes, scales and out must be non-null");
+  if (!aligned16(codes) || !aligned16(out)) return fail(CBQ_EINVAL, "codes and out must be 16-byte aligned");
+
+  cbq::GemmArgs a{};
+  a.codes = codes; a.scales = scales; a.act_bits = act_bits; a.n_rows = n_rows;
+  a.offsets = expert_offsets; a.row_token = row_token;
+  a.w[0] = cbq::GemmW{W[0].idx, W[0].codebook};
+  a.w[1] = n_w == 2 ? cbq::GemmW{W[1].idx, W[1].codebook} : a.w[0];
+  a.n_w = n_w; a.E = W[0].E; a.N = W[0].N; a.K = W[0].K; a.bits = W[0].bits;
+  a.swiglu = epilogue == CBQ_EPI_SWIGLU_BF16;
+  a.out = out; a.ldo = ldo;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (path == CBQ_PATH_LUT) {
+    e = cbq::launch_lut_decode(a, -1, n_rows > CBQ_AUTO_MAX_LUT_ROWS, s);
+  } else if (path == CBQ_PATH_MFMA) {
+    e = cbq::launch_mfma_prefill(a, 0, s);
+  } else {
+    e = cbq::launch_lut_decode(a, CBQ_AUTO_MAX_LUT_ROWS, false, s);
+    if (e == hipSuccess && n_rows > CBQ_AUTO_MAX_LUT_ROWS)
+      e = cbq::launch_mfma_prefill(a, CBQ_AUTO_MAX_LUT_ROWS, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "codebook_lut_gemm launch");
+  return CBQ_OK;
+}
+
+CBQ_EXPORT int cbq_moe_combine(const float* expert_out, const int32_t* slot_of, const float* topk_w,
+                               int64_t T, int32_t topk, int32_t H, int32_t n_shared, float* y,
+                               void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0");
+  if (T > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "T must be < 2^31");
+  if (topk < 1 || topk > 8) return fail(CBQ_EINVAL, "topk must be in [1, 8] (got %d)", topk);
+  if (n_shared < 0 || n_shared > 8) return fail(CBQ_EINVAL, "n_shared must be in [0, 8]");
+  if (H < 4 || H % 4) return fail(CBQ_EINVAL, "H must be a positive multiple of 4 (got %d)", H);
+  if (T == 0) return CBQ_OK;
+  if (!expert_out || !slot_of || !topk_w || !y) return fail(CBQ_EINVAL, "pointers must be non-null");
+  if (!aligned16(expert_out) || !aligned16(y)) return fail(CBQ_EINVAL, "expert_out and y must be 16-byte aligned");
+  hipError_t e = cbq::launch_combine(expert_out, slot_of, topk_w, T, topk, H, n_shared, y,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_combine launch");
+  return CBQ_OK;
+}

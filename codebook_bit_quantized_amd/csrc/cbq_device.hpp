@@ -1,0 +1,193 @@
+// Device-side building blocks shared by the GEMM kernels (gfx950, wave64).
+//
+// Per-row codebook tables live in VGPRs and are looked up with v_perm_b32 byte
+// permutes, so the "one-time LUT precomputation then lookup" of the LUT kernel
+// (CodeQuant2, Figure 4) costs no LDS bandwidth and has no bank conflicts (the
+// problem the AI Radio episode's "Improvements" section describes for an
+// LDS-resident table).
+//
+// A row's 2^bits fp16 centroids are split into a low-byte table and a high-byte
+// table; a lookup selects the low and high bytes of up to four weights with one
+// permute each and interleaves them into fp16 pairs.
+//
+// K order inside a group of eight consecutive weights.  Every dequantiser and every
+// activation converter below emits four dwords per group in the same order
+//     D0 = (k0, k2)  D1 = (k4, k6)  D2 = (k1, k3)  D3 = (k5, k7)
+// (low half first).  Because weights and activations are permuted identically, the
+// dot product over the group is unchanged; only the fp32 summation order differs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cbq {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// v_perm_b32: byte i of the result = byte sel[i] of the 8-byte value {hi:lo}
+// (0..3 from lo, 4..7 from hi; 12 gives 0x00).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, float c) {
+  f16x2 v = __builtin_bit_cast(f16x2, a);
+  f16x2 k = {(_Float16)c, (_Float16)c};
+  return __builtin_bit_cast(uint32_t, v + k);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// Per-row codebook tables in registers.
+//   lo[i] = low bytes of entries 4i..4i+3, hi[i] = their high bytes.
+template <int BITS> struct RowTable {
+  static constexpr int L = 1 << BITS;
+  static constexpr int NT = (L + 3) / 4;
+  uint32_t lo[NT], hi[NT];
+
+  // cb: pointer to the row's 2^BITS fp16 patterns (4-byte aligned).
+  __device__ __forceinline__ void load(const uint16_t* cb) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(cb);
+    if constexpr (BITS == 2) {
+      uint32_t a = w[0], b = w[1];
+      lo[0] = perm(b, a, 0x06040200u);
+      hi[0] = perm(b, a, 0x07050301u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        uint32_t a = w[2 * i], b = w[2 * i + 1];
+        lo[i] = perm(b, a, 0x06040200u);
+        hi[i] = perm(b, a, 0x07050301u);
+      }
+    }
+  }
+};
+
+// 4-bit: one dword of eight nibble indices -> D0..D3.
+__device__ __forceinline__ void dequant4(const RowTable<4>& t, uint32_t x, uint32_t* d) {
+  const uint32_t s7e = x & 0x07070707u;
+  const uint32_t s7o = (x >> 4) & 0x07070707u;
+  const uint32_t be = ((x >> 1) & 0x04040404u) | 0x03020100u;   // byte i -> i + 4*bit3
+  const uint32_t bo = ((x >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t le = perm(perm(t.lo[3], t.lo[2], s7e), perm(t.lo[1], t.lo[0], s7e), be);
+  const uint32_t he = perm(perm(t.hi[3], t.hi[2], s7e), perm(t.hi[1], t.hi[0], s7e), be);
+  const uint32_t lo = perm(perm(t.lo[3], t.lo[2], s7o), perm(t.lo[1], t.lo[0], s7o), bo);
+  const uint32_t ho = perm(perm(t.hi[3], t.hi[2], s7o), perm(t.hi[1], t.hi[0], s7o), bo);
+  d[0] = perm(he, le, 0x05010400u);   // (k0, k2)
+  d[1] = perm(he, le, 0x07030602u);   // (k4, k6)
+  d[2] = perm(ho, lo, 0x05010400u);   // (k1, k3)
+  d[3] = perm(ho, lo, 0x07030602u);   // (k5, k7)
+}
+
+// 3-bit: eight indices in the low 24 bits of f -> D0..D3.
+__device__ __forceinline__ void dequant3(const RowTable<3>& t, uint32_t f, uint32_t* d) {
+  uint32_t ta = (f & 0x3Fu) | ((f << 10) & 0x3F0000u);          // i0,i1 | i2,i3 << 16
+  uint32_t sa = (ta | (ta << 5)) & 0x07070707u;                  // bytes i0 i1 i2 i3
+  uint32_t tb = ((f >> 12) & 0x3Fu) | ((f >> 2) & 0x3F0000u);
+  uint32_t sb = (tb | (tb << 5)) & 0x07070707u;                  // bytes i4 i5 i6 i7
+  const uint32_t la = perm(t.lo[1], t.lo[0], sa), ha = perm(t.hi[1], t.hi[0], sa);
+  const uint32_t lb = perm(t.lo[1], t.lo[0], sb), hb = perm(t.hi[1], t.hi[0], sb);
+  d[0] = perm(ha, la, 0x06020400u);   // (k0, k2)
+  d[1] = perm(hb, lb, 0x06020400u);   // (k4, k6)
+  d[2] = perm(ha, la, 0x07030501u);   // (k1, k3)
+  d[3] = perm(hb, lb, 0x07030501u);   // (k5, k7)
+}
+
+// 2-bit: one dword of sixteen indices -> two groups (D0..D3 of indices 0..7, then 8..15).
+__device__ __forceinline__ void dequant2(const RowTable<2>& t, uint32_t x, uint32_t* d) {
+  const uint32_t y0 = x & 0x03030303u;          // bytes: i0 i4 i8 i12
+  const uint32_t y1 = (x >> 2) & 0x03030303u;   // i1 i5 i9 i13
+  const uint32_t y2 = (x >> 4) & 0x03030303u;   // i2 i6 i10 i14
+  const uint32_t y3 = (x >> 6) & 0x03030303u;   // i3 i7 i11 i15
+  // selector for a pair (a, b): bytes (a, a+4, b, b+4) = (a | b << 16) * 0x101 + 0x04000400
+#define CBQ_SEL2(v) (__umul24((v), 0x101u) + 0x04000400u)
+  d[0] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y2, y0, 0x0C040C00u)));   // (k0, k2)
+  d[1] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y2, y0, 0x0C050C01u)));   // (k4, k6)
+  d[2] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y3, y1, 0x0C040C00u)));   // (k1, k3)
+  d[3] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y3, y1, 0x0C050C01u)));   // (k5, k7)
+  d[4] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y2, y0, 0x0C060C02u)));   // (k8, k10)
+  d[5] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y2, y0, 0x0C070C03u)));   // (k12, k14)
+  d[6] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y3, y1, 0x0C060C02u)));   // (k9, k11)
+  d[7] = perm(t.hi[0], t.lo[0], CBQ_SEL2(perm(y3, y1, 0x0C070C03u)));   // (k13, k15)
+#undef CBQ_SEL2
+}
+
+// Dequantise 32 consecutive indices (one lane's slice: 4*BITS bytes already loaded
+// into w[0..BITS-1]) into 16 dwords: group j (indices 8j..8j+7) -> d[4j..4j+3].
+template <int BITS>
+__device__ __forceinline__ void dequant32(const RowTable<BITS>& t, const uint32_t* w, uint32_t* d) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dequant4(t, w[j], d + 4 * j);
+  } else if constexpr (BITS == 3) {
+    dequant3(t, w[0], d + 0);
+    dequant3(t, __builtin_amdgcn_alignbit(w[1], w[0], 24), d + 4);
+    dequant3(t, __builtin_amdgcn_alignbit(w[2], w[1], 16), d + 8);
+    dequant3(t, w[2] >> 8, d + 12);
+  } else {
+    dequant2(t, w[0], d + 0);
+    dequant2(t, w[1], d + 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Activation codes -> fp16 in the same group order.
+// A4: one dword of eight two's-complement nibbles.  (0x6400 | u) is fp16 1024 + u.
+__device__ __forceinline__ void codes4_to_f16(uint32_t x, uint32_t* d) {
+  const uint32_t xb = x ^ 0x88888888u;          // nibble v -> v + 8
+  const uint32_t e = xb & 0x0F0F0F0Fu;
+  const uint32_t o = (xb >> 4) & 0x0F0F0F0Fu;
+  d[0] = pk_add_f16(perm(0x64646464u, e, 0x04010400u), -1032.0f);
+  d[1] = pk_add_f16(perm(0x64646464u, e, 0x04030402u), -1032.0f);
+  d[2] = pk_add_f16(perm(0x64646464u, o, 0x04010400u), -1032.0f);
+  d[3] = pk_add_f16(perm(0x64646464u, o, 0x04030402u), -1032.0f);
+}
+
+// A8: two dwords holding eight int8 codes k0..k7.
+__device__ __forceinline__ void codes8_to_f16(uint32_t x0, uint32_t x1, uint32_t* d) {
+  const uint32_t b0 = x0 ^ 0x80808080u, b1 = x1 ^ 0x80808080u;   // c -> c + 128
+  d[0] = pk_add_f16(perm(0x64646464u, b0, 0x04020400u), -1152.0f);   // (k0, k2)
+  d[1] = pk_add_f16(perm(0x64646464u, b1, 0x04020400u), -1152.0f);   // (k4, k6)
+  d[2] = pk_add_f16(perm(0x64646464u, b0, 0x04030401u), -1152.0f);   // (k1, k3)
+  d[3] = pk_add_f16(perm(0x64646464u, b1, 0x04030401u), -1152.0f);   // (k5, k7)
+}
+
+// 32 consecutive codes (16 bytes for A4, 32 for A8, in c[0..ABITS-1]) -> 16 dwords.
+template <int ABITS>
+__device__ __forceinline__ void codes32_to_f16(const uint32_t* c, uint32_t* d) {
+  if constexpr (ABITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) codes4_to_f16(c[j], d + 4 * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) codes8_to_f16(c[2 * j], c[2 * j + 1], d + 4 * j);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small numeric helpers
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, ((uint32_t)h) << 16);
+}
+
+// g * u / (1 + exp(-g)) in fp32
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u / (1.0f + expf(-g));
+}
+
+}  // namespace cbq

@@ -1,0 +1,227 @@
+// Codebook-LUT GEMM, decode path (few rows per expert; HBM-bound on the indices).
+//
+// CodeQuant2, Figure 4: the LUT kernel precomputes a table once and then replaces
+// multiplications by table lookups; Figure 3: one codebook per weight row.  Here the
+// one-time precomputation is each row's 2^bits-entry fp16 table, split into low and
+// high bytes and kept in VGPRs for the whole K sweep; a lookup is a v_perm_b32 byte
+// permute (four weights per permute), which never touches LDS and so cannot bank-
+// conflict.  The dequantised weights go straight into the B operand of a 16x16x32
+// fp16 MFMA whose A operand holds up to 16 tokens' activation codes (exact in fp16),
+// so the integer x centroid products are exact and accumulate in fp32.
+//
+// Layout.  A workgroup owns 16 output rows n of one expert and `splitk` waves that
+// split K into 128-channel chunks.  Lane l serves row n0 + (l & 15) and channel
+// slice (l >> 4) * 32 of each chunk, i.e. one 4*bits-byte load per chunk per matrix.
+// Partial sums are reduced through LDS in wave order (deterministic).  Rows of the
+// expert are processed in blocks of 16*MSUB; each block streams the weights once.
+#include "cbq_internal.hpp"
+
+namespace cbq {
+
+template <int BITS>
+__device__ __forceinline__ void load_idx(const uint8_t* p, bool ok, uint32_t* w) {
+  if constexpr (BITS == 4) {
+    u32x4 v = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (BITS == 3) {
+    u32x3 v = ok ? *reinterpret_cast<const u32x3*>(p) : u32x3{0, 0, 0};
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else {
+    u32x2 v = ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0, 0};
+    w[0] = v[0]; w[1] = v[1];
+  }
+}
+
+template <int ABITS>
+__device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t* c) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  u32x4 a = ok ? q[0] : u32x4{0, 0, 0, 0};
+  c[0] = a[0]; c[1] = a[1]; c[2] = a[2]; c[3] = a[3];
+  if constexpr (ABITS == 8) {
+    u32x4 b = ok ? q[1] : u32x4{0, 0, 0, 0};
+    c[4] = b[0]; c[5] = b[1]; c[6] = b[2]; c[7] = b[3];
+  }
+}
+
+// Wide variants (MSUB = 8) always run with a single wave; the others with up to 16.
+template <int BITS, int ABITS, int NW, int MSUB>
+__global__ void __launch_bounds__(MSUB == 8 ? 64 : (NW == 2 ? 512 : 1024))
+lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+                  const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
+                  GemmW w0, GemmW w1, int64_t n_rows, int N, int K, int splitk, int max_rows,
+                  void* __restrict__ out, int64_t ldo) {
+  extern __shared__ f32x4 red[];   // [(splitk-1) * NW * MSUB][64]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int e = blockIdx.y;
+  int64_t r0, me;
+  if (offsets) {
+    r0 = offsets[e];
+    me = offsets[e + 1] - r0;
+  } else {
+    r0 = 0;
+    me = n_rows;
+  }
+  if (me <= 0 || (max_rows >= 0 && me > max_rows)) return;
+
+  const int nl = lane & 15, g = lane >> 4;
+  const int n = blockIdx.x * 16 + nl;
+  const bool nvalid = n < N;
+  const int nn = nvalid ? n : 0;
+  constexpr int L = 1 << BITS;
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  const int64_t code_bytes = (int64_t)K * ABITS / 8;
+
+  RowTable<BITS> tab[NW];
+  const uint8_t* wrow[NW];
+  tab[0].load(w0.codebook + ((int64_t)e * N + nn) * L);
+  wrow[0] = w0.idx + ((int64_t)e * N + nn) * row_bytes;
+  if constexpr (NW == 2) {
+    tab[1].load(w1.codebook + ((int64_t)e * N + nn) * L);
+    wrow[1] = w1.idx + ((int64_t)e * N + nn) * row_bytes;
+  }
+
+  const int nchunks = (K + 127) >> 7;
+  const int cpw = (nchunks + splitk - 1) / splitk;
+  const int c_begin = wave * cpw;
+  const int c_end = min(nchunks, c_begin + cpw);
+
+  for (int64_t mb = 0; mb < me; mb += 16 * MSUB) {
+    f32x4 acc[NW][MSUB];
+    const uint8_t* arow[MSUB];
+    bool aok[MSUB];
+#pragma unroll
+    for (int s = 0; s < MSUB; ++s) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc[w][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int64_t m = mb + s * 16 + nl;
+      aok[s] = m < me;
+      const int64_t r = r0 + (aok[s] ? m : 0);
+      const int64_t tok = row_token ? (int64_t)row_token[r] : r;
+      arow[s] = codes + tok * code_bytes;
+    }
+
+    uint32_t wv[NW][BITS];
+    {
+      const int kb = c_begin * 128 + g * 32;
+      const bool ok = nvalid && c_begin < c_end && kb < K;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) load_idx<BITS>(wrow[w] + (int64_t)kb * BITS / 8, ok, wv[w]);
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+      const int kb = c * 128 + g * 32;
+      const bool kok = kb < K;
+      uint32_t bd[NW][16];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[w], wv[w], bd[w]);
+      // prefetch the next chunk's indices while this chunk computes
+      {
+        const int kn = kb + 128;
+        const bool ok = nvalid && (c + 1 < c_end) && kn < K;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) load_idx<BITS>(wrow[w] + (int64_t)kn * BITS / 8, ok, wv[w]);
+      }
+#pragma unroll
+      for (int s = 0; s < MSUB; ++s) {
+        if (mb + s * 16 >= me) break;
+        uint32_t av[ABITS], ad[16];
+        load_codes<ABITS>(arow[s] + (int64_t)kb * ABITS / 8, aok[s] && kok, av);
+        codes32_to_f16<ABITS>(av, ad);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x8 A = as_f16x8(ad[4 * j], ad[4 * j + 1], ad[4 * j + 2], ad[4 * j + 3]);
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
+            acc[w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[w][s], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ordered split-K reduction
+    if (splitk > 1) {
+      if (wave > 0) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int s = 0; s < MSUB; ++s) red[(((wave - 1) * NW + w) * MSUB + s) * 64 + lane] = acc[w][s];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        for (int v = 1; v < splitk; ++v)
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int s = 0; s < MSUB; ++s) acc[w][s] += red[(((v - 1) * NW + w) * MSUB + s) * 64 + lane];
+      }
+    }
+
+    // epilogue: lane holds D[m = 4*(lane>>4) + i][n = lane & 15]
+    if (wave == 0 && nvalid) {
+#pragma unroll
+      for (int s = 0; s < MSUB; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = mb + s * 16 + 4 * g + i;
+          if (m >= me) continue;
+          const int64_t r = r0 + m;
+          const int64_t tok = row_token ? (int64_t)row_token[r] : r;
+          const float sc = scales[tok];
+          if constexpr (NW == 2) {
+            const float gv = acc[0][s][i] * sc, uv = acc[1][s][i] * sc;
+            reinterpret_cast<uint16_t*>(out)[r * ldo + n] = f32_to_bf16_rne(silu_mul(gv, uv));
+          } else {
+            reinterpret_cast<float*>(out)[r * ldo + n] = acc[0][s][i] * sc;
+          }
+        }
+      }
+    }
+    if (splitk > 1) __syncthreads();
+  }
+}
+
+template <int BITS, int ABITS, int NW, int MSUB>
+static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
+  const int E = a.offsets ? a.E : 1;
+  dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)E);
+  const size_t lds = (size_t)(splitk - 1) * NW * MSUB * 64 * sizeof(f32x4);
+  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB>), grid, dim3(64 * splitk), lds,
+                     stream, a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows,
+                     a.N, a.K, splitk, max_rows, a.out, a.ldo);
+  return hipGetLastError();
+}
+
+template <int BITS, int ABITS>
+static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, bool wide, hipStream_t s) {
+  if (a.n_w == 2)
+    return wide ? launch_t<BITS, ABITS, 2, 8>(a, max_rows, splitk, s)
+                : launch_t<BITS, ABITS, 2, 2>(a, max_rows, splitk, s);
+  return wide ? launch_t<BITS, ABITS, 1, 8>(a, max_rows, splitk, s)
+              : launch_t<BITS, ABITS, 1, 2>(a, max_rows, splitk, s);
+}
+
+hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, bool wide_m, hipStream_t stream) {
+  // split K so the grid holds enough waves to keep HBM busy
+  const int E = a.offsets ? a.E : 1;
+  const int64_t active = a.offsets ? (a.n_rows < E ? a.n_rows : E) : 1;
+  const int64_t tiles = (int64_t)((a.N + 15) / 16) * (active > 0 ? active : 1);
+  const int nchunks = (a.K + 127) / 128;
+  int splitk = 1;
+  if (!wide_m) {
+    while (splitk < 16 && tiles * splitk < 4096 && splitk * 2 <= nchunks) splitk *= 2;
+    if (a.n_w == 2 && splitk > 8) splitk = 8;
+  }
+  const int ab = a.act_bits;
+  switch (a.bits * 10 + (ab == 8 ? 8 : 4)) {
+    case 44: return launch_b<4, 4>(a, max_rows, splitk, wide_m, stream);
+    case 48: return launch_b<4, 8>(a, max_rows, splitk, wide_m, stream);
+    case 34: return launch_b<3, 4>(a, max_rows, splitk, wide_m, stream);
+    case 38: return launch_b<3, 8>(a, max_rows, splitk, wide_m, stream);
+    case 24: return launch_b<2, 4>(a, max_rows, splitk, wide_m, stream);
+    case 28: return launch_b<2, 8>(a, max_rows, splitk, wide_m, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cbq

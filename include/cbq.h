@@ -1,0 +1,196 @@
+/*
+ * cbq.h - codebook-LUT MoE expert path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libcbq.so.  Four calls make one MoE FFN layer of the CodeQuant /
+ * CodeQuant2 method: activations rotated by a Walsh-Hadamard transform and
+ * quantised per token to int4/int8, top-k routing, expert matmuls whose weights are
+ * packed 2/3/4-bit indices into per-output-row fp16 codebooks, and the weighted
+ * combine of expert outputs.
+ *
+ * Conventions shared by every call
+ *  - Every tensor pointer is DEVICE memory owned by the caller; the library never
+ *    allocates, frees or retains device memory.  Pointers must stay valid until the
+ *    work queued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *    queued asynchronously; no call synchronises the host with the device.
+ *  - Arguments are validated on the host before any HIP call.  A violation returns
+ *    CBQ_EINVAL / CBQ_EUNSUPPORTED / CBQ_EWORKSPACE and queues nothing; a failed
+ *    launch returns CBQ_EHIP.  cbq_last_error() then describes the failure (the
+ *    message is per calling thread).  No C++ exception crosses this interface.
+ *  - Empty work (zero tokens or rows) is a successful no-op.  Results for non-finite
+ *    inputs are unspecified.
+ *  - The library keeps no mutable global state; calls on different streams may run
+ *    concurrently.
+ *  - bf16 / fp16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef CBQ_H
+#define CBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CBQ_OK = 0,
+  CBQ_EINVAL = -1,        /* bad pointer, size, layout or alignment */
+  CBQ_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+  CBQ_EWORKSPACE = -3,    /* workspace missing or too small */
+  CBQ_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+};
+
+/* GEMM epilogues */
+enum {
+  CBQ_EPI_F32 = 0,          /* out = fp32 [n_rows][ldo]: y = scale * acc */
+  CBQ_EPI_SWIGLU_BF16 = 1   /* n_w == 2: out = bf16 [n_rows][ldo]: h = silu(g) * u */
+};
+
+/* GEMM inner paths */
+enum {
+  CBQ_PATH_AUTO = 0,  /* per expert: LUT path when its row count <= CBQ_AUTO_MAX_LUT_ROWS,
+                         else the MFMA path; decided on the device */
+  CBQ_PATH_LUT = 1,   /* register codebook lookup feeding 16x16x32 MFMA, weights streamed once
+                         per 128 rows of an expert */
+  CBQ_PATH_MFMA = 2   /* weights dequantised tile by tile into LDS as fp16, 32x32x16 MFMA */
+};
+
+#define CBQ_AUTO_MAX_LUT_ROWS 32
+
+/*
+ * One weight matrix type for E experts (E = 1 for a dense linear).
+ * Reading of CodeQuant2, Figure 3 (right): a centroid matrix with one codebook per
+ * weight row and a per-row assignment of every weight to one of its centroids.
+ *  idx      : [E][N][K*bits/8] bytes.  Row n of expert e is an LSB-first bitstream:
+ *             the index of weight k occupies bits [k*bits, (k+1)*bits).
+ *  codebook : [E][N][1 << bits] fp16 bit patterns; entry c of row n is the value
+ *             of every weight of that row whose index is c (order not assumed).
+ *  W[e][n][k] = codebook[e][n][idx(e, n, k)].
+ *  bits in {2, 3, 4}; K % 32 == 0; N % 16 == 0; both pointers 16-byte aligned.
+ */
+typedef struct {
+  const uint8_t* idx;
+  const uint16_t* codebook;
+  int32_t E, N, K, bits;
+} cbq_weights;
+
+/*
+ * cbq_rotate_quantize - Hadamard rotation fused with per-token absmax quantisation.
+ * Passage: CodeQuant2, Figure 1 (rotation fused into the model to smooth activation
+ * outliers) and Tables 1 and 9 (A4W4 / A8W4 activation settings); CodeQuant
+ * abstract (rotation-based outlier smoothing).
+ *
+ *  x          : bf16 [T][ldx] (ldx >= K, ldx % 8 == 0, 16-byte aligned); row t holds
+ *               one token's K channels.
+ *  had_block  : 0 -> rotation block b = K & -K (largest power of two dividing K);
+ *               otherwise b itself (a power of two dividing K; 1 = no rotation);
+ *               b <= 4096.
+ *  act_bits   : 4 (codes in [-8, 7], Q = 7) or 8 (codes in [-127, 127], Q = 127).
+ *  codes      : [T][K*act_bits/8] bytes, 16-byte aligned.  A4: two's-complement
+ *               nibbles, channel 2j in the low nibble of byte j; A8: int8.
+ *  scales     : fp32 [T].
+ *  precond_violations : optional device uint32 counter (NULL to skip the check);
+ *               incremented once per (token, block) whose nonzero bf16 exponents
+ *               spread more than 45 - log2(b) binades, the bound under which the
+ *               fp64 transform below is exact.
+ *
+ *  Computes u = (I_{K/b} (x) H_b) x exactly (Sylvester order, H[i][j] =
+ *  (-1)^popcount(i & j), no normalisation), then in IEEE fp32:
+ *  v = fp32(u); M = max|v|; s = M / Q; q = clamp(rint_even(v / s));
+ *  scale = s * fp32(1/sqrt(b)).  A token with M == 0 gets codes 0 and scale 0.
+ *  Requires 1 <= K, K % 32 == 0, K <= 16384.
+ */
+int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
+                        int32_t had_block, int32_t act_bits, uint8_t* codes, float* scales,
+                        uint32_t* precond_violations, void* stream);
+
+/*
+ * cbq_moe_route_gather - top-k routing and per-expert row lists.
+ * Passage: the AI Radio episode on CodeQuant (introduction: a router sends each input
+ * to the right expert of the mixture).
+ *
+ *  logits         : fp32 [T][E] router logits (1 <= E <= 256), 16-byte aligned rows
+ *                   are not required.
+ *  topk           : 1 <= topk <= min(E, 8).
+ *  renormalize    : 1 -> weights are a softmax over the k selected logits;
+ *                   0 -> the selected entries of a softmax over all E logits.
+ *  n_shared       : 0 <= n_shared <= 8 always-on experts (weight 1) after the routed ones.
+ *  topk_ids       : int32 [T][topk]: the k largest logits, descending, ties to the
+ *                   lower expert id.
+ *  topk_w         : fp32 [T][topk] routing weights.
+ *  expert_offsets : int32 [E + n_shared + 1]: rows of expert e are
+ *                   [expert_offsets[e], expert_offsets[e+1]); the last entry is
+ *                   T*topk + n_shared*T.
+ *  sorted_tokens  : int32 [T*topk + n_shared*T]: the token of every row, tokens
+ *                   ascending inside an expert; shared expert s owns rows
+ *                   T*topk + s*T + t.
+ *  slot_of        : int32 [T][topk]: the row of token t's j-th choice.
+ *  ws, ws_bytes   : workspace of at least cbq_route_workspace(...) bytes (may be NULL
+ *                   when that is 0).
+ *  All integer outputs are deterministic (no dependence on atomic ordering).
+ *  Requires T <= 2^24.
+ */
+size_t cbq_route_workspace(int64_t T, int32_t E, int32_t topk, int32_t n_shared);
+int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk,
+                         int32_t renormalize, int32_t n_shared, int32_t* topk_ids,
+                         float* topk_w, int32_t* expert_offsets, int32_t* sorted_tokens,
+                         int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * cbq_codebook_lut_gemm - grouped expert GEMM with codebook weights.
+ * Passage: CodeQuant2, Figure 4 (LUT kernel: a one-time table precomputation, then
+ * table lookups from on-chip memory) and Figure 3 (per-row centroid codebooks); the
+ * AI Radio episode, "Improvements" (products looked up instead of recomputed;
+ * shared-memory bank conflicts).
+ *
+ *  codes, scales   : quantised activations from cbq_rotate_quantize: codes
+ *                    [T][K*act_bits/8] (16-byte aligned), scales fp32 [T].
+ *  n_rows          : number of GEMM rows R.
+ *  expert_offsets  : int32 [W->E + 1] row ranges per expert (device), or NULL: all
+ *                    R rows use expert 0.
+ *  row_token       : int32 [R]: row r reads token row_token[r] of codes/scales
+ *                    (sorted_tokens of the router), or NULL: row r reads token r.
+ *  W, n_w          : n_w == 1: one weight set; n_w == 2: {gate, up} with equal
+ *                    E/N/K/bits (host pointer to the array; read during the call only).
+ *  epilogue        : CBQ_EPI_F32 (n_w == 1): out[r][n] = scale[t_r] * sum_k q[t_r][k] W[e][n][k]
+ *                    as fp32.  CBQ_EPI_SWIGLU_BF16 (n_w == 2): g, u as above, then
+ *                    out[r][n] = bf16_rne(silu(g) * u).
+ *  path            : CBQ_PATH_AUTO / CBQ_PATH_LUT / CBQ_PATH_MFMA (results agree within
+ *                    fp32 accumulation order; products are exact in every path).
+ *  out, ldo        : fp32 or bf16 [R][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
+ *  ws, ws_bytes    : workspace of at least cbq_gemm_workspace(...) bytes.
+ *  Rows of experts with no rows, and rows outside every expert range, are not written.
+ */
+size_t cbq_gemm_workspace(const cbq_weights* W, int32_t n_w, int64_t n_rows, int32_t act_bits,
+                          int32_t path);
+int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits,
+                          int64_t n_rows, const int32_t* expert_offsets,
+                          const int32_t* row_token, const cbq_weights* W, int32_t n_w,
+                          int32_t epilogue, int32_t path, void* out, int64_t ldo, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * cbq_moe_combine - weighted sum of the expert outputs per token.
+ * Passage: the AI Radio episode on CodeQuant, introduction (a mixture of experts
+ * with a router); the weighting follows the router's softmax.
+ *
+ *  expert_out : fp32 [T*topk + n_shared*T][H] in row order (16-byte aligned, H % 4 == 0).
+ *  slot_of, topk_w : from cbq_moe_route_gather.
+ *  y          : fp32 [T][H]: y[t] = sum_j topk_w[t][j] * expert_out[slot_of[t][j]]
+ *               (j ascending) + sum_s expert_out[T*topk + s*T + t].
+ */
+int cbq_moe_combine(const float* expert_out, const int32_t* slot_of, const float* topk_w,
+                    int64_t T, int32_t topk, int32_t H, int32_t n_shared, float* y,
+                    void* stream);
+
+/* Name of a status code, and the calling thread's message for its last failure. */
+const char* cbq_status_string(int status);
+const char* cbq_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int cbq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CBQ_H */

@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/cbq.h declares, and reject
+invalid arguments with the documented status before touching HIP, so each error
+path can be exercised on a machine without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cbq.h")
+
+cbq = pytest.importorskip("codebook_bit_quantized_amd")
+
+
+def _lib():
+    if not os.path.exists(cbq.LIB_PATH):
+        pytest.skip("libcbq.so not built")
+    return cbq.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cbq_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared() == sorted(cbq.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.cbq_version() >= 100
+    assert lib.cbq_status_string(cbq.CBQ_EINVAL) == b"CBQ_EINVAL"
+    assert lib.cbq_status_string(123) == b"CBQ_UNKNOWN"
+
+
+class _Fake:
+    """A pointer value that is never dereferenced (validation fails before use)."""
+    P = ctypes.c_void_p(0x1000)
+    UNALIGNED = ctypes.c_void_p(0x1004)
+
+
+def test_rotate_quantize_validation():
+    lib = _lib()
+    P, U = _Fake.P, _Fake.UNALIGNED
+    rq = lib.cbq_rotate_quantize
+    assert rq(P, -1, 256, 256, 0, 4, P, P, None, None) == cbq.CBQ_EINVAL
+    assert rq(P, 4, 250, 256, 0, 4, P, P, None, None) == cbq.CBQ_EINVAL      # K % 32
+    assert b"K" in lib.cbq_last_error()
+    assert rq(P, 4, 32768, 32768, 0, 4, P, P, None, None) == cbq.CBQ_EUNSUPPORTED
+    assert rq(P, 4, 256, 200, 0, 4, P, P, None, None) == cbq.CBQ_EINVAL      # ldx < K
+    assert rq(P, 4, 256, 260, 0, 4, P, P, None, None) == cbq.CBQ_EINVAL      # ldx % 8
+    assert rq(P, 4, 256, 256, 0, 5, P, P, None, None) == cbq.CBQ_EINVAL      # act_bits
+    assert rq(P, 4, 256, 256, 3, 4, P, P, None, None) == cbq.CBQ_EINVAL      # had_block
+    assert rq(P, 4, 384, 384, 256, 4, P, P, None, None) == cbq.CBQ_EINVAL    # 256 does not divide 384
+    assert rq(None, 4, 256, 256, 0, 4, P, P, None, None) == cbq.CBQ_EINVAL   # null x
+    assert rq(U, 4, 256, 256, 0, 4, P, P, None, None) == cbq.CBQ_EINVAL      # misaligned
+    assert rq(None, 0, 256, 256, 0, 4, None, None, None, None) == cbq.CBQ_OK  # T = 0 no-op
+
+
+def test_route_validation():
+    lib = _lib()
+    P = _Fake.P
+    rg = lib.cbq_moe_route_gather
+    assert lib.cbq_route_workspace(64, 128, 8, 0) == 0
+    assert rg(P, 4, 0, 1, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EUNSUPPORTED   # E = 0
+    assert rg(P, 4, 300, 1, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EUNSUPPORTED
+    assert rg(P, 4, 8, 9, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL          # topk > 8
+    assert rg(P, 4, 4, 5, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL          # topk > E
+    assert rg(P, 4, 8, 2, 2, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL          # renormalize
+    assert rg(P, 4, 8, 2, 1, 9, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL          # n_shared
+    assert rg(P, -1, 8, 2, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL
+    assert rg(None, 4, 8, 2, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL       # null logits
+    assert rg(P, 4, 8, 2, 1, 0, P, P, None, P, P, None, 0, None) == cbq.CBQ_EINVAL       # null offsets
+
+
+def _w(E=1, N=64, K=256, bits=4, idx=0x1000, cb=0x2000):
+    return cbq.cbq_weights(idx, cb, E, N, K, bits)
+
+
+def _gemm(lib, W, n_w=1, act_bits=4, n_rows=4, epi=0, path=0, out=0x3000, ldo=64, codes=0x4000):
+    arr = (cbq.cbq_weights * len(W))(*W)
+    return lib.cbq_codebook_lut_gemm(ctypes.c_void_p(codes), ctypes.c_void_p(0x5000), act_bits,
+                                     n_rows, None, None, arr, n_w, epi, path,
+                                     ctypes.c_void_p(out), ldo, None, 0, None)
+
+
+def test_gemm_validation():
+    lib = _lib()
+    E = cbq.CBQ_EINVAL
+    assert _gemm(lib, [_w(bits=5)]) == cbq.CBQ_EUNSUPPORTED
+    assert _gemm(lib, [_w(bits=1)]) == cbq.CBQ_EUNSUPPORTED
+    assert _gemm(lib, [_w(K=100)]) == E
+    assert _gemm(lib, [_w(N=40)]) == E
+    assert _gemm(lib, [_w(E=0)]) == E
+    assert _gemm(lib, [_w(idx=0)]) == E
+    assert _gemm(lib, [_w(idx=0x1004)]) == E                      # misaligned idx
+    assert _gemm(lib, [_w()], act_bits=6) == E
+    assert _gemm(lib, [_w(), _w()], n_w=2, epi=0) == E            # F32 needs one set
+    assert _gemm(lib, [_w()], n_w=1, epi=1) == E                  # SwiGLU needs two
+    assert _gemm(lib, [_w(), _w(N=128)], n_w=2, epi=1) == E       # mismatched gate/up
+    assert _gemm(lib, [_w()], epi=7) == E
+    assert _gemm(lib, [_w()], path=3) == E
+    assert _gemm(lib, [_w()], ldo=32) == E                        # ldo < N
+    assert _gemm(lib, [_w()], ldo=66) == E                        # ldo % 4
+    assert _gemm(lib, [_w()], n_rows=-1) == E
+    assert _gemm(lib, [_w()], out=0) == E                         # null out
+    assert _gemm(lib, [_w()], codes=0x4004) == E                  # misaligned codes
+    assert _gemm(lib, [_w()], n_rows=0) == cbq.CBQ_OK             # empty: no-op
+    assert lib.cbq_gemm_workspace(ctypes.pointer(_w()), 1, 16, 4, 0) == 0
+
+
+def test_combine_validation():
+    lib = _lib()
+    P, U = _Fake.P, _Fake.UNALIGNED
+    cb = lib.cbq_moe_combine
+    assert cb(P, P, P, -1, 2, 64, 0, P, None) == cbq.CBQ_EINVAL
+    assert cb(P, P, P, 4, 0, 64, 0, P, None) == cbq.CBQ_EINVAL
+    assert cb(P, P, P, 4, 9, 64, 0, P, None) == cbq.CBQ_EINVAL
+    assert cb(P, P, P, 4, 2, 62, 0, P, None) == cbq.CBQ_EINVAL
+    assert cb(P, P, P, 4, 2, 64, 9, P, None) == cbq.CBQ_EINVAL
+    assert cb(None, P, P, 4, 2, 64, 0, P, None) == cbq.CBQ_EINVAL
+    assert cb(U, P, P, 4, 2, 64, 0, P, None) == cbq.CBQ_EINVAL
+    assert cb(None, None, None, 0, 2, 64, 0, None, None) == cbq.CBQ_OK
+
+
+def test_error_message_is_per_call():
+    lib = _lib()
+    P = _Fake.P
+    lib.cbq_rotate_quantize(P, 4, 250, 256, 0, 4, P, P, None, None)
+    assert lib.cbq_last_error() != b""
+    lib.cbq_rotate_quantize(None, 0, 256, 256, 0, 4, None, None, None, None)
+    assert lib.cbq_last_error() == b""
