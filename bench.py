@@ -1,0 +1,323 @@
+"""Throughput of the codebook-LUT MoE path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole path (rotate+quantise, route, gate/up GEMM with
+SwiGLU, rotate+quantise of h, down GEMM, combine) over one batch of seeded synthetic
+input.  The default workload is the 64-routed + 2-shared expert layer (hidden 2048,
+FFN 1408, top-6, 3-bit gate/up and 2-bit down codebooks, A4): a 4096-token prefill
+followed by a 32-token decode batch, the one workload that exercises every step of
+the path including both GEMM inner paths.  Inputs are resident in HBM before the
+timed region; the region is bracketed by device synchronisation.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline of the dominant
+kernel (the prefill gate/up GEMM; its duration is measured with HIP events on the
+stream it runs on), the roofline of the decode gate/up GEMM measured separately with
+the caches flushed, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+METRIC = "MoE LUT-GEMM tokens/s + % HBM roofline (decode) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "mfma_prefill": ["codebook_bit_quantized_amd/csrc/lut_gemm_prefill.hip",
+                     "codebook_bit_quantized_amd/csrc/cbq_device.hpp"],
+    "lut_decode": ["codebook_bit_quantized_amd/csrc/lut_gemm_decode.hip",
+                   "codebook_bit_quantized_amd/csrc/cbq_device.hpp"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_hash(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+class MoEPhase:
+    """Device buffers and the call sequence for one MoE layer over T tokens."""
+
+    def __init__(self, cbq, torch, wl, W, x_bits, logits, path_gu, path_dn):
+        self.cbq, self.torch, self.wl, self.W = cbq, torch, wl, W
+        dev = "cuda:0"
+        T, H, F, E, k, S, a = (x_bits.shape[0], wl.H, wl.F, wl.E, wl.topk, wl.n_shared, wl.act_bits)
+        self.T, self.R = T, T * k + S * T
+        self.x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.logits = torch.from_numpy(logits).to(dev)
+        self.codes = torch.empty((T, H * a // 8), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((T,), dtype=torch.float32, device=dev)
+        self.rt = dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                       weights=torch.empty((T, k), dtype=torch.float32, device=dev),
+                       offsets=torch.empty((E + S + 1,), dtype=torch.int32, device=dev),
+                       sorted_tokens=torch.empty((self.R,), dtype=torch.int32, device=dev),
+                       slot_of=torch.empty((T, k), dtype=torch.int32, device=dev))
+        self.h = torch.empty((self.R, F), dtype=torch.bfloat16, device=dev)
+        self.codes_h = torch.empty((self.R, F * a // 8), dtype=torch.uint8, device=dev)
+        self.scales_h = torch.empty((self.R,), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.R, H), dtype=torch.float32, device=dev)
+        self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.path_gu, self.path_dn = path_gu, path_dn
+        self.ev = None   # (start, end) events around the gate/up GEMM when timing it
+
+    def run(self, stream=None):
+        cbq, wl, W = self.cbq, self.wl, self.W
+        a = wl.act_bits
+        cbq.rotate_quantize(self.x, a, codes=self.codes, scales=self.scales, stream=stream)
+        cbq.moe_route_gather(self.logits, wl.topk, True, wl.n_shared, out=self.rt, stream=stream)
+        if self.ev is not None:
+            self.ev[0].record()
+        cbq.codebook_lut_gemm(self.codes, self.scales, a, [W["gate"], W["up"]],
+                              n_rows=self.R, expert_offsets=self.rt["offsets"],
+                              row_token=self.rt["sorted_tokens"], path=self.path_gu, out=self.h,
+                              stream=stream)
+        if self.ev is not None:
+            self.ev[1].record()
+        cbq.rotate_quantize(self.h, a, codes=self.codes_h, scales=self.scales_h, stream=stream)
+        cbq.codebook_lut_gemm(self.codes_h, self.scales_h, a, [W["down"]], n_rows=self.R,
+                              expert_offsets=self.rt["offsets"], path=self.path_dn, out=self.out,
+                              stream=stream)
+        cbq.moe_combine(self.out, self.rt["slot_of"], self.rt["weights"], wl.n_shared, y=self.y,
+                        stream=stream)
+
+    def gemm_gu_only(self):
+        self.cbq.codebook_lut_gemm(self.codes, self.scales, self.wl.act_bits,
+                                   [self.W["gate"], self.W["up"]], n_rows=self.R,
+                                   expert_offsets=self.rt["offsets"],
+                                   row_token=self.rt["sorted_tokens"], path=self.path_gu,
+                                   out=self.h)
+
+
+def choose_path(cbq, counts, routed_E):
+    """The path AUTO would give every expert with rows, made explicit so each GEMM is
+    one kernel launch (AUTO also launches the other path's grid, which then exits)."""
+    active = counts[counts > 0]
+    if active.size == 0 or active.max() <= cbq.AUTO_MAX_LUT_ROWS:
+        return cbq.PATH_LUT
+    if active.min() > cbq.AUTO_MAX_LUT_ROWS:
+        return cbq.PATH_MFMA
+    return cbq.PATH_AUTO
+
+
+def gate_up_bytes(wl, counts, T):
+    """Algorithmic HBM bytes of one gate/up launch: each active expert's gate and up
+    indices + codebooks once, the token codes and scales once, h written once."""
+    per_matrix = wl.F * wl.H * wl.bits_gate_up // 8 + wl.F * (1 << wl.bits_gate_up) * 2
+    n_active = int((counts > 0).sum())
+    R = int(counts.sum())
+    return (2 * per_matrix * n_active + T * (wl.H * wl.act_bits // 8 + 4) + R * 4 + R * wl.F * 2)
+
+
+def gate_up_flops(wl, counts):
+    return 2.0 * 2.0 * float(counts.sum()) * wl.F * wl.H
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(wl, weights_np, prefill_sample: int, decode_T: int):
+    """Time the oracle (as it stands) on a bounded sample of the workload on this host."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    gate, up, down = weights_np
+    t0 = time.perf_counter()
+    ntok = 0
+    for T, dec in ((prefill_sample, False), (decode_T, True)):
+        x, lg = datagen.moe_tokens(wl, T if not dec else decode_T, decode=dec)
+        if not dec:
+            x, lg = x[:prefill_sample], lg[:prefill_sample]
+        oracle.moe_layer(x, lg, gate, up, down, wl.topk, wl.n_shared, wl.act_bits)
+        ntok += x.shape[0]
+    dt = time.perf_counter() - t0
+    return dict(value=ntok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"oracle MoE layer on the first {prefill_sample} prefill tokens plus the "
+                       f"{decode_T}-token decode batch ({ntok} tokens, {dt:.1f} s, numpy fp64, "
+                       f"BLAS threads {threads})")
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="moe64s2_h2048_f1408")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-prefill-sample", type=int, default=256)
+    ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for calibrating HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(experts would shard across GPUs; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import codebook_bit_quantized_amd as cbq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cbq.load_library()
+    dev = "cuda:0"
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+        return
+
+    wl = datagen.WORKLOADS[args.workload]
+    if wl.kind != "moe":
+        print("bench.py: the default measurement covers MoE workloads", file=sys.stderr)
+        sys.exit(1)
+    t_setup = time.perf_counter()
+    gate_np, up_np, down_np = datagen.moe_weights(wl)
+
+    def upw(ws):
+        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
+                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
+                                   K=ws.K, bits=ws.bits)
+
+    W = dict(gate=upw(gate_np), up=upw(up_np), down=upw(down_np))
+    phases_T = list(wl.T_list)
+    phases = []
+    for i, T in enumerate(phases_T):
+        decode = (len(phases_T) == 2 and i == 1)
+        x, lg = datagen.moe_tokens(wl, T, decode=decode)
+        ph = MoEPhase(cbq, torch, wl, W, x, lg, cbq.PATH_AUTO, cbq.PATH_AUTO)
+        ph.run()
+        torch.cuda.synchronize()
+        offs = ph.rt["offsets"].cpu().numpy().astype(np.int64)
+        counts = np.diff(offs)
+        ph.counts = counts
+        ph.path_gu = ph.path_dn = choose_path(cbq, counts, wl.E)
+        ph.decode = decode or T <= 64
+        phases.append(ph)
+    setup_s = time.perf_counter() - t_setup
+
+    # dominant kernel: the gate/up GEMM of the largest phase
+    dom = max(phases, key=lambda p: p.R)
+    start_evs, end_evs = [], []
+
+    for _ in range(args.warmup):
+        for ph in phases:
+            ph.run()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dom.ev = (s, e)
+        for ph in phases:
+            ph.run()
+        start_evs.append(s)
+        end_evs.append(e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom.ev = None
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    tokens = sum(p.T for p in phases)
+    value = tokens / (ms_per_step / 1000.0)
+    dom_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(start_evs, end_evs)]))
+
+    dom_flops = gate_up_flops(wl, dom.counts)
+    achieved = dom_flops / (dom_ms / 1000.0) / 1e12
+    kernel = "mfma_prefill" if dom.path_gu == cbq.PATH_MFMA else "lut_decode"
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=F16_MFMA_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / F16_MFMA_PEAK_TFLOPS, 4),
+                    traffic=read_traffic(kernel, wl.name),
+                    kernel=f"{kernel} gate/up+SwiGLU", avg_launch_us=round(dom_ms * 1000.0, 2),
+                    algorithmic_flops=dom_flops)
+
+    # decode gate/up GEMM roofline, cold caches (flush > MALL between reps)
+    decode_info = None
+    dec = [p for p in phases if p.decode and p is not dom]
+    if dec:
+        p = dec[0]
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        times = []
+        for _ in range(args.decode_reps):
+            flush.fill_(1.0)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            p.gemm_gu_only()
+            e.record()
+            torch.cuda.synchronize()
+            times.append(s.elapsed_time(e))
+        del flush
+        d_ms = float(np.median(times))
+        d_bytes = gate_up_bytes(wl, p.counts, p.T)
+        gbs = d_bytes / (d_ms / 1000.0) / 1e9
+        decode_info = dict(tokens=p.T, bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
+                           unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                           traffic=read_traffic("lut_decode", wl.name),
+                           kernel="lut_decode gate/up+SwiGLU (caches flushed)",
+                           median_launch_us=round(d_ms * 1000.0, 2), algorithmic_bytes=d_bytes,
+                           active_experts=int((p.counts > 0).sum()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, (gate_np, up_np, down_np), args.cpu_prefill_sample,
+                           phases_T[1] if len(phases_T) > 1 else 32)
+
+    cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
+               hidden=wl.H, ffn=wl.F, experts=wl.E, shared_experts=wl.n_shared, topk=wl.topk,
+               bits_gate_up=wl.bits_gate_up, bits_down=wl.bits_down, act_bits=wl.act_bits,
+               paths={str(p.T): int(p.path_gu) for p in phases})
+    line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,
+                roofline=roofline, decode_roofline=decode_info, cpu_baseline=cpu,
+                setup_s=round(setup_s, 1), host=platform.node())
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
