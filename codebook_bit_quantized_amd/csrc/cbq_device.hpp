@@ -173,6 +173,41 @@ __device__ __forceinline__ void codes32_to_f16(const uint32_t* c, uint32_t* d) {
   }
 }
 
+// Buffer-resource loads.  A load whose byte offset is at or past num_records returns
+// zeros without faulting, so a disabled load is just an out-of-range offset and no
+// select has to touch the loaded registers (which would force an early wait).
+constexpr uint32_t kOffNone = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BYTES>
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+  if constexpr (BYTES == 16) {
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (BYTES == 12) {
+    u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else if constexpr (BYTES == 8) {
+    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    static_assert(BYTES == 4, "unsupported load width");
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes every wave wait for its outstanding global loads (prefetches
+// included) at each barrier; this one waits only for the wave's own LDS traffic.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // small numeric helpers
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -188,6 +223,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // g * u / (1 + exp(-g)) in fp32
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * u / (1.0f + expf(-g));
+}
+
+// Same with the hardware exp2 and reciprocal (a few ulp in fp32; the result is then
+// rounded to bf16, whose spacing is 2^16 fp32 ulps).
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 }  // namespace cbq

@@ -1,203 +1,278 @@
 // Codebook GEMM, prefill path (many rows per expert: a dense contraction).
 //
-// Once an expert has enough rows, each dequantised weight is reused by many tokens,
-// so the work becomes MFMA-bound: weights are dequantised tile by tile into LDS as
-// fp16 (exact: the centroids are fp16) with the same per-row register tables as the
-// decode path, activation codes are converted to fp16 (exact), and 32x32x16 fp16
-// MFMAs accumulate in fp32.  Products are exact; only the fp32 summation order
-// differs from the plain definition.
+// Once an expert has enough rows, every dequantised weight is reused by many tokens
+// and the work becomes MFMA-bound.  Weights are dequantised with the same per-row
+// register tables as the decode path (CodeQuant2, Figure 4: a one-time table
+// precomputation followed by lookups), and go straight into the B operand of
+// 32x32x16 fp16 MFMAs: the 32 consecutive indices one lane loads per 64-channel step
+// are exactly the 4 x 8 values its B fragments need, so weights never pass through
+// LDS.  Activation codes are converted to fp16 once per step into LDS and shared by
+// the four waves.  Products are exact (int codes x fp16 centroids); only the fp32
+// summation order differs from the plain definition.
 //
-// Tile: 128 rows (tokens of one expert) x 128 columns x 64 channels per step, 256
-// threads as 2x2 waves of 64x64.  For the gate/up pair the 128 columns are 64 gate
-// rows and the same 64 up rows, so the SwiGLU epilogue finds g and u in one lane.
-// Thread t dequantises 32 weights of column t/2 and converts 32 codes of row t/2 per
-// step; LDS is double-buffered so the next step's loads overlap this step's MFMAs.
-// Workgroup (x, y) takes column tile x and the y-th 128-row tile in expert order,
+// Tile: up to 256 rows of one expert x 256 columns x 64 channels per step.  Wave w
+// owns 64 columns (for the gate/up pair: 32 gate rows and the same 32 up rows, so
+// the SwiGLU epilogue finds g and u in one lane) and all rows of the tile, held as
+// up to 8 x 2 accumulators of 32x32 (256 AGPRs, one wave per SIMD).  Only the
+// 32-row sub-tiles that hold rows are computed, so an expert's last tile wastes
+// fewer than 32 rows.  A is double-buffered in LDS and the next step's loads are
+// issued before this step's MFMAs.
+//
+// Workgroup (x, y) takes column tile x and the y-th 256-row tile in expert order,
 // skipping experts with at most min_rows rows (those go to the decode path).
 #include "cbq_internal.hpp"
 
 namespace cbq {
 
 namespace {
-constexpr int BM = 128;
-constexpr int BNC = 128;   // columns per tile
-constexpr int BK = 64;
+constexpr int BM = 256;     // rows per tile
+constexpr int BK = 64;      // channels per step
 constexpr int LDW = BK + 8; // fp16 per LDS row (padding staggers the banks)
+constexpr int MSUB = BM / 32;
 
-template <int BITS>
-__device__ __forceinline__ void load_idx_p(const uint8_t* p, bool ok, uint32_t* w) {
-  if constexpr (BITS == 4) {
-    u32x4 v = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-  } else if constexpr (BITS == 3) {
-    u32x3 v = ok ? *reinterpret_cast<const u32x3*>(p) : u32x3{0, 0, 0};
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
-  } else {
-    u32x2 v = ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0, 0};
-    w[0] = v[0]; w[1] = v[1];
-  }
-}
-
-template <int ABITS>
-__device__ __forceinline__ void load_codes_p(const uint8_t* p, bool ok, uint32_t* c) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  u32x4 a = ok ? q[0] : u32x4{0, 0, 0, 0};
-  c[0] = a[0]; c[1] = a[1]; c[2] = a[2]; c[3] = a[3];
-  if constexpr (ABITS == 8) {
-    u32x4 b = ok ? q[1] : u32x4{0, 0, 0, 0};
-    c[4] = b[0]; c[5] = b[1]; c[6] = b[2]; c[7] = b[3];
-  }
-}
 }  // namespace
 
+// Everything a tile needs after scheduling; shared by the per-NMS K-loops.
+template <int BITS, int ABITS>
+struct TileCtx {
+  __amdgpu_buffer_rsrc_t wres[2];   // this expert's index block of each matrix
+  __amdgpu_buffer_rsrc_t cres;      // the activation codes
+  uint32_t wrow_off[2];             // byte offset of this lane's weight rows
+  uint32_t crow_off;                // byte offset of this thread's activation row
+  bool nvalid[2];
+  int nrow[2];
+  RowTable<BITS> tab[2];
+  bool avalid;
+  int K, g, nl, tid, rows;
+};
+
+template <int BITS, int ABITS, int NW, int NMS>
+__device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t (*As)[BM * LDW],
+                                         const float* s_scale, const int64_t* s_row,
+                                         void* __restrict__ out, int64_t ldo) {
+  const int K = c.K, g = c.g, nl = c.nl, tid = c.tid;
+  f32x16 acc[NMS][2];
+#pragma unroll
+  for (int i = 0; i < NMS; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][s][v] = 0.0f;
+  const int nk = (K + BK - 1) / BK;
+  // Raw loads run two steps ahead in a ring of two slots; the step loop is unrolled
+  // by two so every slot index is a compile-time constant.
+  uint32_t rw[2][2][BITS];     // [slot][matrix] raw indices
+  uint32_t ra[2][ABITS * 2];   // [slot] raw activation codes
+  uint32_t bdA[2][16], bdB[2][16];  // dequantised weights, alternating between steps
+  f16x8 af[NMS];               // A fragments of the current 16-channel sub-step
+
+  auto gload = [&](int kt, uint32_t (&w)[2][BITS], uint32_t* a) {
+    const bool live = kt < nk;
+    const int kb = kt * BK + g * 32;
+    const bool kok = live && kb < K;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      buf_load<4 * BITS>(c.wres[s], (c.nvalid[s] && kok) ? c.wrow_off[s] + (uint32_t)(kb * BITS / 8) : kOffNone, w[s]);
+    const int ka = kt * BK;
+    const bool ok0 = live && c.avalid, ok1 = ok0 && ka + 32 < K;
+    const uint32_t ab = c.crow_off + (uint32_t)(ka * ABITS / 8);
+#pragma unroll
+    for (int i = 0; i < ABITS / 4; ++i)       // first 32 codes
+      buf_load<16>(c.cres, ok0 ? ab + 16 * i : kOffNone, a + 4 * i);
+#pragma unroll
+    for (int i = 0; i < ABITS / 4; ++i)       // second 32 codes
+      buf_load<16>(c.cres, ok1 ? ab + 16 * (ABITS / 4 + i) : kOffNone, a + 4 * (ABITS / 4 + i));
+  };
+  auto astore = [&](int buf, const uint32_t* a) {
+    uint32_t d[16];
+    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][tid * LDW]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      codes32_to_f16<ABITS>(a + h * ABITS, d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ap[h * 4 + j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+    }
+  };
+  auto frag = [&](int buf, int kk, int ms) {
+    return *reinterpret_cast<const f16x8*>(&As[buf][(ms * 32 + nl) * LDW + g * 32 + kk * 8]);
+  };
+  // One step: MFMAs on LDS buffer `buf` with weights `bd`, while step kt+1 is
+  // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
+  // (wf, af_raw) is refilled with step kt+2.
+  auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
+                  uint32_t (&wn)[2][BITS], uint32_t* an, uint32_t (&wf)[2][BITS], uint32_t* af_raw) {
+    gload(kt + 2, wf, af_raw);
+    __builtin_amdgcn_sched_barrier(0);        // keep the refill at the top of the step
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const f16x8 b0 = as_f16x8(bd[0][4 * kk], bd[0][4 * kk + 1], bd[0][4 * kk + 2], bd[0][4 * kk + 3]);
+      const f16x8 b1 = as_f16x8(bd[1][4 * kk], bd[1][4 * kk + 1], bd[1][4 * kk + 2], bd[1][4 * kk + 3]);
+#pragma unroll
+      for (int ms = 0; ms < NMS; ++ms) {
+        acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
+        acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
+        if (kk < 3) af[ms] = frag(buf, kk + 1, ms);
+      }
+    }
+    astore(buf ^ 1, an);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) dequant32<BITS>(c.tab[s], wn[s], bn[s]);
+    // interleave: after each MFMA a few VALU ops of the next step's preparation and,
+    // every other MFMA, the next sub-step's read of the fragment just consumed
+#pragma unroll
+    for (int i = 0; i < 8 * NMS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      if ((i & 1) && i < 6 * NMS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms) af[ms] = frag(buf ^ 1, 0, ms);
+  };
+
+  gload(0, rw[0], ra[0]);
+  gload(1, rw[1], ra[1]);
+  astore(0, ra[0]);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) dequant32<BITS>(c.tab[s], rw[0][s], bdA[s]);
+  lds_barrier();
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms) af[ms] = frag(0, 0, ms);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0, bdA, bdB, rw[1], ra[1], rw[0], ra[0]);       // prepare kt+1 from slot 1
+    step(kt + 1, 1, bdB, bdA, rw[0], ra[0], rw[1], ra[1]);   // prepare kt+2 from slot 0
+  }
+  if (kt < nk) step(kt, 0, bdA, bdB, rw[1], ra[1], rw[0], ra[0]);
+
+  // ---- epilogue: acc[ms][s][v] = D[ms*32 + 8*(v/4) + 4*g + v%4][nl] ----
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int mloc = ms * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (mloc >= c.rows) continue;
+      const int64_t r = s_row[mloc];
+      const float sc = s_scale[mloc];
+      if constexpr (NW == 2) {
+        if (c.nvalid[0]) {
+          const float gv = acc[ms][0][v] * sc, uv = acc[ms][1][v] * sc;
+          reinterpret_cast<uint16_t*>(out)[r * ldo + c.nrow[0]] = f32_to_bf16_rne(silu_mul_fast(gv, uv));
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (c.nvalid[s]) reinterpret_cast<float*>(out)[r * ldo + c.nrow[s]] = acc[ms][s][v] * sc;
+      }
+    }
+  }
+}
+
 template <int BITS, int ABITS, int NW>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 1)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
                     void* __restrict__ out, int64_t ldo) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BNC * LDW];
+  __shared__ float s_scale[BM];
+  __shared__ int64_t s_row[BM];
   __shared__ int64_t s_r0, s_me, s_m0;
   __shared__ int s_e;
 
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int64_t ty = blockIdx.y;
-    int found = -1;
-    int64_t r0 = 0, me = 0, m0 = 0;
+  // ---- tile -> (expert, first row): wave 0 scans the experts' tile counts ----
+  if (tid < 64) {
+    const int64_t ty = blockIdx.y;
     if (!offsets) {
-      if (ty * BM < n_rows) { found = 0; r0 = 0; me = n_rows; m0 = ty * BM; }
+      if (tid == 0) {
+        const bool ok = ty * BM < n_rows;
+        s_e = ok ? 0 : -1; s_r0 = 0; s_me = n_rows; s_m0 = ty * BM;
+      }
     } else {
-      for (int e = 0; e < E; ++e) {
-        const int64_t a = offsets[e], c = offsets[e + 1] - offsets[e];
-        if (c <= min_rows) continue;
-        const int64_t nt = (c + BM - 1) / BM;
-        if (ty < nt) { found = e; r0 = a; me = c; m0 = ty * BM; break; }
-        ty -= nt;
+      if (tid == 0) s_e = -1;
+      int64_t before = 0;                            // tiles of earlier 64-expert chunks
+      for (int base = 0; base < E; base += 64) {
+        const int ex = base + tid;
+        int64_t a = 0, cnt = 0;
+        if (ex < E) { a = offsets[ex]; cnt = offsets[ex + 1] - a; }
+        const int64_t nt = cnt > min_rows ? (cnt + BM - 1) / BM : 0;
+        int64_t incl = nt;                           // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int64_t o = __shfl_up(incl, d);
+          if (tid >= d) incl += o;
+        }
+        const int64_t lo = before + incl - nt;
+        if (nt > 0 && ty >= lo && ty < lo + nt) {
+          s_e = ex; s_r0 = a; s_me = cnt; s_m0 = (ty - lo) * BM;
+        }
+        before += __shfl(incl, 63);
+        if (before > ty) break;
       }
     }
-    s_e = found; s_r0 = r0; s_me = me; s_m0 = m0;
   }
   __syncthreads();
   const int e = s_e;
   if (e < 0) return;
   const int64_t r0 = s_r0, me = s_me, m0 = s_m0;
+  const int rows = (int)((me - m0) < BM ? (me - m0) : BM);
+  const int nms = (rows + 31) >> 5;                  // 32-row sub-tiles holding rows
 
-  constexpr int NCOL = (NW == 2) ? BNC / 2 : BNC;    // weight rows per matrix in the tile
+  TileCtx<BITS, ABITS> c;
+  c.K = K;
+  c.tid = tid;
+  c.rows = rows;
+  // ---- activation loader: thread t owns tile row t ----
+  c.avalid = tid < rows;
+  int64_t atok = 0;
+  if (c.avalid) {
+    const int64_t r = r0 + m0 + tid;
+    atok = row_token ? (int64_t)row_token[r] : r;
+    s_scale[tid] = scales[atok];
+    s_row[tid] = r;
+  }
+  c.cres = make_rsrc(codes, 0x7FFFFFFFu);
+  c.crow_off = (uint32_t)(atok * ((int64_t)K * ABITS / 8));
+
+  // ---- weight rows of this lane ----
+  const int lane = tid & 63, wave = tid >> 6;
+  c.nl = lane & 31;
+  c.g = lane >> 5;
+  constexpr int NCOL = (NW == 2) ? 128 : 256;        // weight rows per matrix per tile
   const int n0 = blockIdx.x * NCOL;
+  if constexpr (NW == 2) { c.nrow[0] = c.nrow[1] = n0 + wave * 32 + c.nl; }   // gate, up
+  else { c.nrow[0] = n0 + wave * 64 + c.nl; c.nrow[1] = c.nrow[0] + 32; }
   constexpr int L = 1 << BITS;
   const int64_t row_bytes = (int64_t)K * BITS / 8;
-  const int64_t code_bytes = (int64_t)K * ABITS / 8;
-
-  // ---- loader roles ----
-  const int col = tid >> 1, khalf = tid & 1;
-  const int wsel = (NW == 2) ? (col / NCOL) : 0;
-  const int n = n0 + ((NW == 2) ? (col % NCOL) : col);
-  const bool nvalid = n < N;
-  const GemmW W = (NW == 2 && wsel == 1) ? w1 : w0;
-  RowTable<BITS> tab;
-  tab.load(W.codebook + ((int64_t)e * N + (nvalid ? n : 0)) * L);
-  const uint8_t* wrow = W.idx + ((int64_t)e * N + (nvalid ? n : 0)) * row_bytes;
-
-  const int arow = tid >> 1;
-  const bool avalid = m0 + arow < me;
-  const int64_t ar = r0 + m0 + (avalid ? arow : 0);
-  const int64_t atok = row_token ? (int64_t)row_token[ar] : ar;
-  const uint8_t* crow = codes + atok * code_bytes;
-
-  uint32_t wv[BITS], av[ABITS];
-  auto gload = [&](int kt) {
-    const int kb = kt * BK + khalf * 32;
-    const bool kok = kb < K;
-    load_idx_p<BITS>(wrow + (int64_t)kb * BITS / 8, nvalid && kok, wv);
-    load_codes_p<ABITS>(crow + (int64_t)kb * ABITS / 8, avalid && kok, av);
-  };
-  auto lstore = [&](int buf) {
-    uint32_t d[16];
-    dequant32<BITS>(tab, wv, d);
-    u32x4* bp = reinterpret_cast<u32x4*>(&Bs[buf][col * LDW + khalf * 32]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bp[j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
-    codes32_to_f16<ABITS>(av, d);
-    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][arow * LDW + khalf * 32]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ap[j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
-  };
-
-  // ---- MFMA roles ----
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int cb[2];
-  if constexpr (NW == 2) { cb[0] = wn * 32; cb[1] = NCOL + wn * 32; }   // gate, up
-  else { cb[0] = wn * 64; cb[1] = wn * 64 + 32; }
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      f16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const f16x8*>(&As[buf][(wm * 64 + i * 32 + lr) * LDW + kk * 16 + lk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const f16x8*>(&Bs[buf][(cb[j] + lr) * LDW + kk * 16 + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+  for (int s = 0; s < 2; ++s) {
+    const GemmW& W = (NW == 2 && s == 1) ? w1 : w0;
+    c.nvalid[s] = c.nrow[s] < N;
+    const int64_t rowi = (int64_t)e * N + (c.nvalid[s] ? c.nrow[s] : 0);
+    c.tab[s].load(W.codebook + rowi * L);
+    c.wres[s] = make_rsrc(W.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
+    c.wrow_off[s] = (uint32_t)((c.nvalid[s] ? c.nrow[s] : 0) * row_bytes);
   }
 
-  // ---- epilogue: acc[i][j][v] = D[8*(v/4) + 4*(lane/32) + v%4][lane%32] ----
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int mloc = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const int64_t m = m0 + mloc;
-      if (m >= me) continue;
-      const int64_t r = r0 + m;
-      const int64_t tok = row_token ? (int64_t)row_token[r] : r;
-      const float sc = scales[tok];
-      if constexpr (NW == 2) {
-        const int nn = n0 + wn * 32 + lr;
-        if (nn < N) {
-          const float gv = acc[i][0][v] * sc, uv = acc[i][1][v] * sc;
-          reinterpret_cast<uint16_t*>(out)[r * ldo + nn] = f32_to_bf16_rne(silu_mul(gv, uv));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int nn = n0 + cb[j] + lr;
-          if (nn < N) reinterpret_cast<float*>(out)[r * ldo + nn] = acc[i][j][v] * sc;
-        }
-      }
-    }
+  switch (nms) {
+    case 1: tile_run<BITS, ABITS, NW, 1>(c, As, s_scale, s_row, out, ldo); break;
+    case 2: tile_run<BITS, ABITS, NW, 2>(c, As, s_scale, s_row, out, ldo); break;
+    case 3: tile_run<BITS, ABITS, NW, 3>(c, As, s_scale, s_row, out, ldo); break;
+    case 4: tile_run<BITS, ABITS, NW, 4>(c, As, s_scale, s_row, out, ldo); break;
+    case 5: tile_run<BITS, ABITS, NW, 5>(c, As, s_scale, s_row, out, ldo); break;
+    case 6: tile_run<BITS, ABITS, NW, 6>(c, As, s_scale, s_row, out, ldo); break;
+    case 7: tile_run<BITS, ABITS, NW, 7>(c, As, s_scale, s_row, out, ldo); break;
+    default: tile_run<BITS, ABITS, NW, 8>(c, As, s_scale, s_row, out, ldo); break;
   }
 }
 
 template <int BITS, int ABITS>
 static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
-  const int ncol = a.n_w == 2 ? BNC / 2 : BNC;
+  const int ncol = a.n_w == 2 ? 128 : 256;
   const int64_t mtiles = (a.n_rows + BM - 1) / BM + (a.offsets ? E : 0);
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
