@@ -138,6 +138,15 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   if (n_rows > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "n_rows must be < 2^31");
   if (ldo < W[0].N || ldo % 4) return fail(CBQ_EINVAL, "ldo must be >= N and a multiple of 4 (got %lld)", (long long)ldo);
   if (n_rows == 0) return CBQ_OK;
+  {
+    const int64_t esz = epilogue == CBQ_EPI_SWIGLU_BF16 ? 2 : 4;
+    if (n_rows * ldo * esz >= (int64_t(1) << 30))
+      return fail(CBQ_EUNSUPPORTED, "output must be smaller than 1 GiB per call (n_rows * ldo * %lld bytes)", (long long)esz);
+    if ((int64_t)W[0].N * W[0].K * W[0].bits / 8 >= (int64_t(1) << 31))
+      return fail(CBQ_EUNSUPPORTED, "one expert's index block must be smaller than 2 GiB");
+    if (!row_token && n_rows * ((int64_t)W[0].K * act_bits / 8) >= (int64_t(1) << 31))
+      return fail(CBQ_EUNSUPPORTED, "codes must be smaller than 2 GiB");
+  }
   if (!codes || !scales || !out) return fail(CBQ_EINVAL, "codes, scales and out must be non-null");
   if (!aligned16(codes) || !aligned16(out)) return fail(CBQ_EINVAL, "codes and out must be 16-byte aligned");
 

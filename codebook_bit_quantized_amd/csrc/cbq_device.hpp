@@ -177,26 +177,40 @@ __device__ __forceinline__ void codes32_to_f16(const uint32_t* c, uint32_t* d) {
 // zeros without faulting, so a disabled load is just an out-of-range offset and no
 // select has to touch the loaded registers (which would force an early wait).
 constexpr uint32_t kOffNone = 0x80000000u;
+// Second sentinel for offsets built as row part + column part: rows use kOffNone,
+// columns kOffCol, so no sum of the two wraps below 2^30 (buffers stay < 1 GiB).
+constexpr uint32_t kOffCol = 0x40000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// off: per-lane byte offset (kOffNone disables the load); soff: wave-uniform byte
+// offset added on top (kept in an SGPR, so advancing it costs no vector ALU work).
 template <int BYTES>
-__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w,
+                                         uint32_t soff = 0) {
   if constexpr (BYTES == 16) {
-    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else if constexpr (BYTES == 12) {
-    u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, soff, 0);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
   } else if constexpr (BYTES == 8) {
-    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
     w[0] = v[0]; w[1] = v[1];
   } else {
     static_assert(BYTES == 4, "unsupported load width");
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
   }
+}
+
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_u16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global
@@ -210,10 +224,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------
 // small numeric helpers
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

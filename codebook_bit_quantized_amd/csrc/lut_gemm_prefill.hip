@@ -48,8 +48,8 @@ struct TileCtx {
 
 template <int BITS, int ABITS, int NW, int NMS>
 __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t (*As)[BM * LDW],
-                                         const float* s_scale, const int64_t* s_row,
-                                         void* __restrict__ out, int64_t ldo) {
+                                         const float* s_scale, const uint32_t* s_rowoff,
+                                         __amdgpu_buffer_rsrc_t ores) {
   const int K = c.K, g = c.g, nl = c.nl, tid = c.tid;
   f32x16 acc[NMS][2];
 #pragma unroll
@@ -98,38 +98,55 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   };
   // One step: MFMAs on LDS buffer `buf` with weights `bd`, while step kt+1 is
   // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
-  // (wf, af_raw) is refilled with step kt+2.
+  // (wf, af_raw) is refilled with step kt+2.  Sub-steps 0-2 run before the barrier
+  // (with the activation conversion and the first matrix's dequantisation); sub-step
+  // 3 runs after it from fragments already in registers, so the next step's first
+  // fragment reads (which need the barrier) overlap MFMAs instead of stalling.
   auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
                   uint32_t (&wn)[2][BITS], uint32_t* an, uint32_t (&wf)[2][BITS], uint32_t* af_raw) {
     gload(kt + 2, wf, af_raw);
     __builtin_amdgcn_sched_barrier(0);        // keep the refill at the top of the step
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 3; ++kk) {
       const f16x8 b0 = as_f16x8(bd[0][4 * kk], bd[0][4 * kk + 1], bd[0][4 * kk + 2], bd[0][4 * kk + 3]);
       const f16x8 b1 = as_f16x8(bd[1][4 * kk], bd[1][4 * kk + 1], bd[1][4 * kk + 2], bd[1][4 * kk + 3]);
 #pragma unroll
       for (int ms = 0; ms < NMS; ++ms) {
         acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
         acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
-        if (kk < 3) af[ms] = frag(buf, kk + 1, ms);
+        af[ms] = frag(buf, kk + 1, ms);
       }
     }
     astore(buf ^ 1, an);
+    dequant32<BITS>(c.tab[0], wn[0], bn[0]);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) dequant32<BITS>(c.tab[s], wn[s], bn[s]);
-    // interleave: after each MFMA a few VALU ops of the next step's preparation and,
-    // every other MFMA, the next sub-step's read of the fragment just consumed
-#pragma unroll
-    for (int i = 0; i < 8 * NMS; ++i) {
+    for (int i = 0; i < 6 * NMS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      if ((i & 1) && i < 6 * NMS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
     __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
+    {
+      const f16x8 b0 = as_f16x8(bd[0][12], bd[0][13], bd[0][14], bd[0][15]);
+      const f16x8 b1 = as_f16x8(bd[1][12], bd[1][13], bd[1][14], bd[1][15]);
 #pragma unroll
-    for (int ms = 0; ms < NMS; ++ms) af[ms] = frag(buf ^ 1, 0, ms);
+      for (int ms = 0; ms < NMS; ++ms) {
+        acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
+        acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
+        af[ms] = frag(buf ^ 1, 0, ms);
+      }
+    }
+    dequant32<BITS>(c.tab[1], wn[1], bn[1]);
+#pragma unroll
+    for (int i = 0; i < 2 * NMS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   gload(0, rw[0], ra[0]);
@@ -148,23 +165,29 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   if (kt < nk) step(kt, 0, bdA, bdB, rw[1], ra[1], rw[0], ra[0]);
 
   // ---- epilogue: acc[ms][s][v] = D[ms*32 + 8*(v/4) + 4*g + v%4][nl] ----
+  // Stores go through a buffer resource: rows past the tile (kOffNone) and columns
+  // past N (kOffCol) carry out-of-range offsets and are dropped without branches.
+  constexpr uint32_t ESZ = NW == 2 ? 2 : 4;
+  uint32_t coff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) coff[s] = c.nvalid[s] ? (uint32_t)c.nrow[s] * ESZ : kOffCol;
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int mloc = ms * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (mloc >= c.rows) continue;
-      const int64_t r = s_row[mloc];
-      const float sc = s_scale[mloc];
-      if constexpr (NW == 2) {
-        if (c.nvalid[0]) {
-          const float gv = acc[ms][0][v] * sc, uv = acc[ms][1][v] * sc;
-          reinterpret_cast<uint16_t*>(out)[r * ldo + c.nrow[0]] = f32_to_bf16_rne(silu_mul_fast(gv, uv));
-        }
-      } else {
+    for (int q = 0; q < 4; ++q) {
+      const int m0 = ms * 32 + 8 * q + 4 * g;            // rows m0 .. m0+3 of this lane
+      const u32x4 ro = *reinterpret_cast<const u32x4*>(&s_rowoff[m0]);
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(&s_scale[m0]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          if (c.nvalid[s]) reinterpret_cast<float*>(out)[r * ldo + c.nrow[s]] = acc[ms][s][v] * sc;
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * q + j;
+        if constexpr (NW == 2) {
+          const float gv = acc[ms][0][v] * sc[j], uv = acc[ms][1][v] * sc[j];
+          buf_store_u16(ores, ro[j] + coff[0], f32_to_bf16_rne(silu_mul_fast(gv, uv)));
+        } else {
+#pragma unroll
+          for (int s = 0; s < 2; ++s) buf_store_f32(ores, ro[j] + coff[s], acc[ms][s][v] * sc[j]);
+        }
       }
     }
   }
@@ -177,8 +200,8 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
                     void* __restrict__ out, int64_t ldo) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDW];
-  __shared__ float s_scale[BM];
-  __shared__ int64_t s_row[BM];
+  __shared__ __attribute__((aligned(16))) float s_scale[BM];
+  __shared__ __attribute__((aligned(16))) uint32_t s_rowoff[BM];   // byte offset of each row in out
   __shared__ int64_t s_r0, s_me, s_m0;
   __shared__ int s_e;
 
@@ -228,11 +251,14 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // ---- activation loader: thread t owns tile row t ----
   c.avalid = tid < rows;
   int64_t atok = 0;
+  constexpr uint32_t ESZ = NW == 2 ? 2 : 4;
+  s_rowoff[tid] = kOffNone;
+  s_scale[tid] = 0.0f;
   if (c.avalid) {
     const int64_t r = r0 + m0 + tid;
     atok = row_token ? (int64_t)row_token[r] : r;
     s_scale[tid] = scales[atok];
-    s_row[tid] = r;
+    s_rowoff[tid] = (uint32_t)(r * ldo * ESZ);
   }
   c.cres = make_rsrc(codes, 0x7FFFFFFFu);
   c.crow_off = (uint32_t)(atok * ((int64_t)K * ABITS / 8));
@@ -257,15 +283,17 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
     c.wrow_off[s] = (uint32_t)((c.nvalid[s] ? c.nrow[s] : 0) * row_bytes);
   }
 
+  // output buffer: every row of this call (n_rows) x ldo elements
+  const __amdgpu_buffer_rsrc_t ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
   switch (nms) {
-    case 1: tile_run<BITS, ABITS, NW, 1>(c, As, s_scale, s_row, out, ldo); break;
-    case 2: tile_run<BITS, ABITS, NW, 2>(c, As, s_scale, s_row, out, ldo); break;
-    case 3: tile_run<BITS, ABITS, NW, 3>(c, As, s_scale, s_row, out, ldo); break;
-    case 4: tile_run<BITS, ABITS, NW, 4>(c, As, s_scale, s_row, out, ldo); break;
-    case 5: tile_run<BITS, ABITS, NW, 5>(c, As, s_scale, s_row, out, ldo); break;
-    case 6: tile_run<BITS, ABITS, NW, 6>(c, As, s_scale, s_row, out, ldo); break;
-    case 7: tile_run<BITS, ABITS, NW, 7>(c, As, s_scale, s_row, out, ldo); break;
-    default: tile_run<BITS, ABITS, NW, 8>(c, As, s_scale, s_row, out, ldo); break;
+    case 1: tile_run<BITS, ABITS, NW, 1>(c, As, s_scale, s_rowoff, ores); break;
+    case 2: tile_run<BITS, ABITS, NW, 2>(c, As, s_scale, s_rowoff, ores); break;
+    case 3: tile_run<BITS, ABITS, NW, 3>(c, As, s_scale, s_rowoff, ores); break;
+    case 4: tile_run<BITS, ABITS, NW, 4>(c, As, s_scale, s_rowoff, ores); break;
+    case 5: tile_run<BITS, ABITS, NW, 5>(c, As, s_scale, s_rowoff, ores); break;
+    case 6: tile_run<BITS, ABITS, NW, 6>(c, As, s_scale, s_rowoff, ores); break;
+    case 7: tile_run<BITS, ABITS, NW, 7>(c, As, s_scale, s_rowoff, ores); break;
+    default: tile_run<BITS, ABITS, NW, 8>(c, As, s_scale, s_rowoff, ores); break;
   }
 }
 

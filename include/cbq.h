@@ -161,6 +161,9 @@ int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk
  *  out, ldo        : fp32 or bf16 [R][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
  *  ws, ws_bytes    : workspace of at least cbq_gemm_workspace(...) bytes.
  *  Rows of experts with no rows, and rows outside every expert range, are not written.
+ *  Limits (CBQ_EUNSUPPORTED beyond them): the output is smaller than 1 GiB, one
+ *  expert's index block and the codes array are smaller than 2 GiB each (the codes
+ *  limit is checked only when row_token is NULL; otherwise it is the caller's).
  */
 size_t cbq_gemm_workspace(const cbq_weights* W, int32_t n_w, int64_t n_rows, int32_t act_bits,
                           int32_t path);
