@@ -52,7 +52,7 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
                   void* __restrict__ out, int64_t ldo) {
   extern __shared__ f32x4 red[];   // [(splitk-1) * NW * MSUB][64]
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = blockIdx.y;
   int64_t r0, me;
   if (offsets) {
@@ -71,15 +71,18 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   constexpr int L = 1 << BITS;
   const int64_t row_bytes = (int64_t)K * BITS / 8;
   const int64_t code_bytes = (int64_t)K * ABITS / 8;
+  (void)L;
 
   RowTable<BITS> tab[NW];
-  const uint8_t* wrow[NW];
+  __amdgpu_buffer_rsrc_t wres[NW];
+  const uint32_t wlane = nvalid ? (uint32_t)(n * row_bytes) + (uint32_t)(g * 4 * BITS) : kOffNone;
   tab[0].load(w0.codebook + ((int64_t)e * N + nn) * L);
-  wrow[0] = w0.idx + ((int64_t)e * N + nn) * row_bytes;
+  wres[0] = make_rsrc(w0.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
   if constexpr (NW == 2) {
     tab[1].load(w1.codebook + ((int64_t)e * N + nn) * L);
-    wrow[1] = w1.idx + ((int64_t)e * N + nn) * row_bytes;
+    wres[1] = make_rsrc(w1.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
   }
+  const __amdgpu_buffer_rsrc_t cres = make_rsrc(codes, 0x7FFFFFFFu);
 
   const int nchunks = (K + 127) >> 7;
   const int cpw = (nchunks + splitk - 1) / splitk;
@@ -88,45 +91,50 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
 
   for (int64_t mb = 0; mb < me; mb += 16 * MSUB) {
     f32x4 acc[NW][MSUB];
-    const uint8_t* arow[MSUB];
-    bool aok[MSUB];
+    uint32_t aoff[MSUB];     // byte offset of this lane's activation row per sub-tile
 #pragma unroll
     for (int s = 0; s < MSUB; ++s) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) acc[w][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const int64_t m = mb + s * 16 + nl;
-      aok[s] = m < me;
-      const int64_t r = r0 + (aok[s] ? m : 0);
-      const int64_t tok = row_token ? (int64_t)row_token[r] : r;
-      arow[s] = codes + tok * code_bytes;
-    }
-
-    uint32_t wv[NW][BITS];
-    {
-      const int kb = c_begin * 128 + g * 32;
-      const bool ok = nvalid && c_begin < c_end && kb < K;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) load_idx<BITS>(wrow[w] + (int64_t)kb * BITS / 8, ok, wv[w]);
-    }
-    for (int c = c_begin; c < c_end; ++c) {
-      const int kb = c * 128 + g * 32;
-      const bool kok = kb < K;
-      uint32_t bd[NW][16];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[w], wv[w], bd[w]);
-      // prefetch the next chunk's indices while this chunk computes
-      {
-        const int kn = kb + 128;
-        const bool ok = nvalid && (c + 1 < c_end) && kn < K;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) load_idx<BITS>(wrow[w] + (int64_t)kn * BITS / 8, ok, wv[w]);
+      uint32_t o = kOffNone;
+      if (m < me) {
+        const int64_t r = r0 + m;
+        const int64_t tok = row_token ? (int64_t)row_token[r] : r;
+        o = (uint32_t)(tok * code_bytes) + (uint32_t)(g * 4 * ABITS);
       }
+      aoff[s] = o;
+    }
+    const int nsub = (int)min<int64_t>((me - mb + 15) >> 4, MSUB);
+
+    // ring of two chunks of raw data, loaded two chunks ahead
+    struct Slot {
+      uint32_t w[NW][BITS];
+      uint32_t a[MSUB][ABITS];
+    };
+    Slot ring[2];
+    auto load = [&](int c, Slot& d) {
+      const bool ok = c < c_end && c * 128 + g * 32 < K;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        buf_load<4 * BITS>(wres[w], ok ? wlane : kOffNone, d.w[w], (uint32_t)(c * 128 * BITS / 8));
+      const uint32_t cs = (uint32_t)(c * 128 * ABITS / 8);
 #pragma unroll
       for (int s = 0; s < MSUB; ++s) {
-        if (mb + s * 16 >= me) break;
-        uint32_t av[ABITS], ad[16];
-        load_codes<ABITS>(arow[s] + (int64_t)kb * ABITS / 8, aok[s] && kok, av);
-        codes32_to_f16<ABITS>(av, ad);
+#pragma unroll
+        for (int h = 0; h < ABITS / 4; ++h)
+          buf_load<16>(cres, ok ? aoff[s] + 16 * h : kOffNone, &d.a[s][4 * h], cs);
+      }
+    };
+    auto chunk = [&](const Slot& cur) {
+      uint32_t bd[NW][16];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[w], cur.w[w], bd[w]);
+#pragma unroll
+      for (int s = 0; s < MSUB; ++s) {
+        if (s >= nsub) break;
+        uint32_t ad[16];
+        codes32_to_f16<ABITS>(cur.a[s], ad);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f16x8 A = as_f16x8(ad[4 * j], ad[4 * j + 1], ad[4 * j + 2], ad[4 * j + 3]);
@@ -137,7 +145,17 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
           }
         }
       }
+    };
+    load(c_begin, ring[0]);
+    load(c_begin + 1, ring[1]);
+    int c = c_begin;
+    for (; c + 1 < c_end; c += 2) {
+      chunk(ring[0]);
+      load(c + 2, ring[0]);
+      chunk(ring[1]);
+      load(c + 3, ring[1]);
     }
+    if (c < c_end) chunk(ring[0]);
 
     // ordered split-K reduction
     if (splitk > 1) {
@@ -209,7 +227,7 @@ hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, bool wide_m, hipSt
   const int nchunks = (a.K + 127) / 128;
   int splitk = 1;
   if (!wide_m) {
-    while (splitk < 16 && tiles * splitk < 4096 && splitk * 2 <= nchunks) splitk *= 2;
+    while (splitk < 16 && tiles * splitk < 16384 && splitk * 2 <= nchunks) splitk *= 2;
     if (a.n_w == 2 && splitk > 8) splitk = 8;
   }
   const int ab = a.act_bits;
