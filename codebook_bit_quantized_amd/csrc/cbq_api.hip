@@ -161,11 +161,11 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (path == CBQ_PATH_LUT) {
-    e = cbq::launch_lut_decode(a, -1, n_rows > CBQ_AUTO_MAX_LUT_ROWS, s);
+    e = cbq::launch_lut_decode(a, -1, s);
   } else if (path == CBQ_PATH_MFMA) {
     e = cbq::launch_mfma_prefill(a, 0, s);
   } else {
-    e = cbq::launch_lut_decode(a, CBQ_AUTO_MAX_LUT_ROWS, false, s);
+    e = cbq::launch_lut_decode(a, CBQ_AUTO_MAX_LUT_ROWS, s);
     if (e == hipSuccess && n_rows > CBQ_AUTO_MAX_LUT_ROWS)
       e = cbq::launch_mfma_prefill(a, CBQ_AUTO_MAX_LUT_ROWS, s);
   }

@@ -39,7 +39,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int topk, int ren
                         int32_t* sorted_tokens, int32_t* slot_of, hipStream_t stream);
 
 // LUT (decode) path.  max_rows >= 0: experts with more rows are skipped (AUTO split).
-hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, bool wide_m, hipStream_t stream);
+hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream);
 
 // MFMA (prefill) path.  Experts with at most min_rows rows are skipped (AUTO split).
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream);

@@ -9,11 +9,16 @@
 // fp16 MFMA whose A operand holds up to 16 tokens' activation codes (exact in fp16),
 // so the integer x centroid products are exact and accumulate in fp32.
 //
-// Layout.  A workgroup owns 16 output rows n of one expert and `splitk` waves that
-// split K into 128-channel chunks.  Lane l serves row n0 + (l & 15) and channel
-// slice (l >> 4) * 32 of each chunk, i.e. one 4*bits-byte load per chunk per matrix.
-// Partial sums are reduced through LDS in wave order (deterministic).  Rows of the
-// expert are processed in blocks of 16*MSUB; each block streams the weights once.
+// Layout.  A workgroup owns 16 output rows n of one expert and `splitk` waves.  Lane l
+// serves row n0 + (l & 15) and channel slice (l >> 4) * 32 of each 128-channel chunk,
+// i.e. one 4*bits-byte load per chunk per matrix.  Rows of the expert are processed
+// in blocks of 32 (two 16-row MFMA sub-tiles sharing each dequantised weight).
+//  - An expert with at most 32 rows (decode) is split along K: wave w takes a range
+//    of chunks, and the partial sums are reduced through LDS in wave order
+//    (deterministic).  This multiplies the loads in flight per output row.
+//  - A larger expert is split along rows: wave w takes row blocks w, w + splitk, ...
+//    over all of K; the waves of a workgroup read the same index bytes at about the
+//    same time, so the repeats are served by the caches.
 #include "cbq_internal.hpp"
 
 namespace cbq {
@@ -43,9 +48,8 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t* 
   }
 }
 
-// Wide variants (MSUB = 8) always run with a single wave; the others with up to 16.
 template <int BITS, int ABITS, int NW, int MSUB>
-__global__ void __launch_bounds__(MSUB == 8 ? 64 : (NW == 2 ? 512 : 1024))
+__global__ void __launch_bounds__(NW == 2 ? 512 : 1024)
 lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                   GemmW w0, GemmW w1, int64_t n_rows, int N, int K, int splitk, int max_rows,
@@ -85,11 +89,15 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   const __amdgpu_buffer_rsrc_t cres = make_rsrc(codes, 0x7FFFFFFFu);
 
   const int nchunks = (K + 127) >> 7;
-  const int cpw = (nchunks + splitk - 1) / splitk;
-  const int c_begin = wave * cpw;
+  const bool rowsplit = splitk > 1 && me > 16 * MSUB;   // uniform over the workgroup
+  const bool ksplit = splitk > 1 && !rowsplit;
+  const int cpw = ksplit ? (nchunks + splitk - 1) / splitk : nchunks;
+  const int c_begin = ksplit ? wave * cpw : 0;
   const int c_end = min(nchunks, c_begin + cpw);
+  const int64_t mb_first = rowsplit ? (int64_t)wave * 16 * MSUB : 0;
+  const int64_t mb_step = rowsplit ? (int64_t)splitk * 16 * MSUB : 16 * MSUB;
 
-  for (int64_t mb = 0; mb < me; mb += 16 * MSUB) {
+  for (int64_t mb = mb_first; mb < me; mb += mb_step) {
     f32x4 acc[NW][MSUB];
     uint32_t aoff[MSUB];     // byte offset of this lane's activation row per sub-tile
 #pragma unroll
@@ -158,7 +166,7 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     if (c < c_end) chunk(ring[0]);
 
     // ordered split-K reduction
-    if (splitk > 1) {
+    if (ksplit) {
       if (wave > 0) {
 #pragma unroll
         for (int w = 0; w < NW; ++w)
@@ -176,7 +184,7 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     }
 
     // epilogue: lane holds D[m = 4*(lane>>4) + i][n = lane & 15]
-    if (wave == 0 && nvalid) {
+    if ((wave == 0 || rowsplit) && nvalid) {
 #pragma unroll
       for (int s = 0; s < MSUB; ++s) {
 #pragma unroll
@@ -195,7 +203,7 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
         }
       }
     }
-    if (splitk > 1) __syncthreads();
+    if (ksplit) __syncthreads();
   }
 }
 
@@ -211,33 +219,28 @@ static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStrea
 }
 
 template <int BITS, int ABITS>
-static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, bool wide, hipStream_t s) {
-  if (a.n_w == 2)
-    return wide ? launch_t<BITS, ABITS, 2, 8>(a, max_rows, splitk, s)
-                : launch_t<BITS, ABITS, 2, 2>(a, max_rows, splitk, s);
-  return wide ? launch_t<BITS, ABITS, 1, 8>(a, max_rows, splitk, s)
-              : launch_t<BITS, ABITS, 1, 2>(a, max_rows, splitk, s);
+static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStream_t s) {
+  if (a.n_w == 2) return launch_t<BITS, ABITS, 2, 2>(a, max_rows, splitk, s);
+  return launch_t<BITS, ABITS, 1, 2>(a, max_rows, splitk, s);
 }
 
-hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, bool wide_m, hipStream_t stream) {
-  // split K so the grid holds enough waves to keep HBM busy
+hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream) {
+  // enough waves per grid to keep HBM busy: split K (small experts) or rows (large)
   const int E = a.offsets ? a.E : 1;
   const int64_t active = a.offsets ? (a.n_rows < E ? a.n_rows : E) : 1;
   const int64_t tiles = (int64_t)((a.N + 15) / 16) * (active > 0 ? active : 1);
   const int nchunks = (a.K + 127) / 128;
   int splitk = 1;
-  if (!wide_m) {
-    while (splitk < 16 && tiles * splitk < 16384 && splitk * 2 <= nchunks) splitk *= 2;
-    if (a.n_w == 2 && splitk > 8) splitk = 8;
-  }
+  while (splitk < 16 && tiles * splitk < 16384 && splitk * 2 <= nchunks) splitk *= 2;
+  if (a.n_w == 2 && splitk > 8) splitk = 8;
   const int ab = a.act_bits;
   switch (a.bits * 10 + (ab == 8 ? 8 : 4)) {
-    case 44: return launch_b<4, 4>(a, max_rows, splitk, wide_m, stream);
-    case 48: return launch_b<4, 8>(a, max_rows, splitk, wide_m, stream);
-    case 34: return launch_b<3, 4>(a, max_rows, splitk, wide_m, stream);
-    case 38: return launch_b<3, 8>(a, max_rows, splitk, wide_m, stream);
-    case 24: return launch_b<2, 4>(a, max_rows, splitk, wide_m, stream);
-    case 28: return launch_b<2, 8>(a, max_rows, splitk, wide_m, stream);
+    case 44: return launch_b<4, 4>(a, max_rows, splitk, stream);
+    case 48: return launch_b<4, 8>(a, max_rows, splitk, stream);
+    case 34: return launch_b<3, 4>(a, max_rows, splitk, stream);
+    case 38: return launch_b<3, 8>(a, max_rows, splitk, stream);
+    case 24: return launch_b<2, 4>(a, max_rows, splitk, stream);
+    case 28: return launch_b<2, 8>(a, max_rows, splitk, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -51,8 +51,9 @@ enum {
 enum {
   CBQ_PATH_AUTO = 0,  /* per expert: LUT path when its row count <= CBQ_AUTO_MAX_LUT_ROWS,
                          else the MFMA path; decided on the device */
-  CBQ_PATH_LUT = 1,   /* register codebook lookup feeding 16x16x32 MFMA, weights streamed once
-                         per 128 rows of an expert */
+  CBQ_PATH_LUT = 1,   /* register codebook lookup feeding 16x16x32 MFMA; an expert's weights
+                         are streamed from HBM once (K split over waves for experts of at most
+                         32 rows, row blocks of 32 split over waves for larger ones) */
   CBQ_PATH_MFMA = 2   /* weights dequantised tile by tile into LDS as fp16, 32x32x16 MFMA */
 };
 
