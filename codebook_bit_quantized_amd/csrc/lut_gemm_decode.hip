@@ -231,7 +231,7 @@ hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream
   const int64_t tiles = (int64_t)((a.N + 15) / 16) * (active > 0 ? active : 1);
   const int nchunks = (a.K + 127) / 128;
   int splitk = 1;
-  while (splitk < 16 && tiles * splitk < 16384 && splitk * 2 <= nchunks) splitk *= 2;
+  while (splitk < 16 && tiles * splitk < 4096 && splitk * 2 <= nchunks) splitk *= 2;
   if (a.n_w == 2 && splitk > 8) splitk = 8;
   const int ab = a.act_bits;
   switch (a.bits * 10 + (ab == 8 ? 8 : 4)) {

@@ -18,8 +18,8 @@
 // fewer than 32 rows.  A is double-buffered in LDS and the next step's loads are
 // issued before this step's MFMAs.
 //
-// Workgroup (x, y) takes column tile x and the y-th 256-row tile in expert order,
-// skipping experts with at most min_rows rows (those go to the decode path).
+// A tile is one column range x the y-th 256-row slice in expert order, skipping
+// experts with at most min_rows rows (those go to the decode path).
 #include "cbq_internal.hpp"
 
 namespace cbq {
@@ -206,9 +206,19 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   __shared__ int s_e;
 
   const int tid = threadIdx.x;
-  // ---- tile -> (expert, first row): wave 0 scans the experts' tile counts ----
+  // ---- workgroup -> tile (M-tile ty, column tile tcol) ----
+  // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so XCD x
+  // gets ids x, x + 8, ...  In round q those ids take one M-tile of the group
+  // 8q .. 8q + 7, with all its column tiles in a row: the column tiles of one M-tile
+  // read the same activation rows and find them in the same L2.  The XCD of each
+  // slot in the group rotates with q, so an expert's full and partial M-tiles do not
+  // pile up on the same XCDs.  (The host makes the M-tile slots a multiple of 8.)
+  const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const uint32_t q = (lin / 8) / gridDim.x;
+  const int64_t ty = (int64_t)((lin % 8 + q) % 8) + 8 * (int64_t)q;
+  const int tcol = (int)((lin / 8) % gridDim.x);
+  // ---- M-tile -> (expert, first row): wave 0 scans the experts' tile counts ----
   if (tid < 64) {
-    const int64_t ty = blockIdx.y;
     if (!offsets) {
       if (tid == 0) {
         const bool ok = ty * BM < n_rows;
@@ -268,7 +278,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   c.nl = lane & 31;
   c.g = lane >> 5;
   constexpr int NCOL = (NW == 2) ? 128 : 256;        // weight rows per matrix per tile
-  const int n0 = blockIdx.x * NCOL;
+  const int n0 = tcol * NCOL;
   if constexpr (NW == 2) { c.nrow[0] = c.nrow[1] = n0 + wave * 32 + c.nl; }   // gate, up
   else { c.nrow[0] = n0 + wave * 64 + c.nl; c.nrow[1] = c.nrow[0] + 32; }
   constexpr int L = 1 << BITS;
@@ -301,7 +311,8 @@ template <int BITS, int ABITS>
 static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
   const int ncol = a.n_w == 2 ? 128 : 256;
-  const int64_t mtiles = (a.n_rows + BM - 1) / BM + (a.offsets ? E : 0);
+  int64_t mtiles = (a.n_rows + BM - 1) / BM + (a.offsets ? E : 0);   // M-tile slots
+  mtiles = (mtiles + 7) / 8 * 8;                     // a multiple of 8 (XCD interleave)
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2>), grid, dim3(256), 0, stream, a.codes,
