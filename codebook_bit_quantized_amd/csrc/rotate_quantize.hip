@@ -3,31 +3,109 @@
 // CodeQuant2, Figure 1: the rotation that smooths activation outliers is fused into
 // the model; Tables 1 and 9: activations are quantised to 4 or 8 bits (A4W4, A8W4).
 //
-// One workgroup per token row.  Each thread owns R consecutive channels (one 16- or
-// 32-byte load).  The transform runs in fp64, which is exact for bf16 inputs whose
-// nonzero exponents in a block spread at most 45 - log2(b) binades: in-thread
-// butterflies for strides < R, lane shuffles for strides up to 64*R, and LDS
-// exchanges across waves beyond that.  The quantiser then follows one fixed IEEE
-// fp32 sequence (round v = fp32(u), s = M / Q, q = rint_even(v / s)), so the codes
-// are reproducible bit for bit.
+// Each thread owns 32 consecutive channels of one token (four 16-byte loads).  A
+// token takes G lanes, G the power of two >= K/32 when K <= 2048 (then 64/G tokens
+// share a wave), else a whole workgroup of ceil(K/2048) waves.  The transform runs
+// in fp64, which is exact for bf16 inputs whose nonzero exponents in a block spread
+// at most 45 - log2(b) binades: five butterfly stages inside the thread, then one
+// lane exchange per further stage (DPP for lane distances 1, 2 and 8, ds_swizzle for
+// 4 and 16, a permute for 32) and LDS exchanges across waves beyond 64 lanes.
+//
+// The quantiser follows one fixed IEEE fp32 sequence: v = fp32(u), M = max|v|,
+// s = M / Q, r = fp32(v / s), q = clamp(rint_even(r)).  The quotient is formed as
+// fp64(v) * fp64(1 / s) and then rounded to fp32: for fp32 v and s the exact quotient
+// is never an fp32 rounding midpoint and lies at least 2^-49 (relative) away from
+// one, while the fp64 product is within 2^-52 of it, so the fp32 rounding, and hence
+// q, is that of the correctly rounded division.
 #include "cbq_internal.hpp"
 
 namespace cbq {
 
-template <int R>
-__device__ __forceinline__ void load_row(const uint16_t* __restrict__ src, bool active, double* v) {
-  if constexpr (R == 8) {
-    u32x4 p = active ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+namespace {
+
+// value of lane (lane ^ M), M a power of two below 64
+template <int M>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);    // quad_perm 1,0,3,2
+  else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  else if constexpr (M == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101F);              // xor 4 in 32 lanes
+  else if constexpr (M == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); // row_ror 8
+  else if constexpr (M == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);             // xor 16 in 32 lanes
+  else return __shfl_xor(v, 32);
+}
+
+template <int M>
+__device__ __forceinline__ double xor_lane_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)xor_lane<M>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)xor_lane<M>((int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+template <int M>
+__device__ __forceinline__ float xor_lane_f32(float v) {
+  return __builtin_bit_cast(float, xor_lane<M>(__builtin_bit_cast(int, v)));
+}
+
+// one butterfly stage between lanes j and j ^ M (M lanes = 32 * M channels apart)
+template <int M>
+__device__ __forceinline__ void lane_stage(double* v, bool upper) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = (double)__builtin_bit_cast(float, p[i] << 16);
-      v[2 * i + 1] = (double)__builtin_bit_cast(float, p[i] & 0xFFFF0000u);
-    }
+  for (int i = 0; i < 32; ++i) {
+    const double p = xor_lane_f64<M>(v[i]);
+    v[i] = upper ? (p - v[i]) : (v[i] + p);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void minmax_lanes(int& emin, int& emax) {
+  emin = min(emin, xor_lane<M>(emin));
+  emax = max(emax, xor_lane<M>(emax));
+}
+
+// floor(log2|x|) of a nonzero channel -> running (min, max)
+__device__ __forceinline__ void exp_range(double x, int& emin, int& emax) {
+  const float f = (float)x;   // exact: x came from bf16
+  if (f != 0.0f) {
+    const int e = __builtin_amdgcn_frexp_expf(f) - 1;
+    emin = min(emin, e);
+    emax = max(emax, e);
+  }
+}
+
+}  // namespace
+
+// G: lanes per token (a power of two <= 64, or a multiple of 64 = the workgroup).
+__global__ void __launch_bounds__(512)
+rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, int K, int logb,
+                       int G, int act_bits, float c_b, uint8_t* __restrict__ codes,
+                       float* __restrict__ scales, uint32_t* __restrict__ precond) {
+  extern __shared__ double xchg[];          // cross-wave butterflies: [8][blockDim]
+  __shared__ float red_max[8];
+  __shared__ int red_emin[8], red_emax[8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nthr = K >> 5;
+  int64_t t;
+  int j;                                     // thread index within the token
+  if (G <= 64) {
+    const int tpw = 64 / G;                  // tokens per wave
+    t = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * tpw + lane / G;
+    j = lane & (G - 1);
   } else {
-    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    t = blockIdx.x;
+    j = tid;
+  }
+  const bool active = t < T && j < nthr;
+  const int b = 1 << logb;
+
+  double v[32];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (active ? t * ldx + (int64_t)j * 32 : 0));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 p = active ? s4[h] : u32x4{0, 0, 0, 0};
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 p = active ? src[h] : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[8 * h + 2 * i] = (double)__builtin_bit_cast(float, p[i] << 16);
@@ -35,77 +113,53 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ src, bool 
       }
     }
   }
-}
-
-// floor(log2|x|) of the nonzero channels -> running (min, max)
-__device__ __forceinline__ void exp_range(double x, int& emin, int& emax) {
-  float f = (float)x;   // exact: x came from bf16
-  if (f != 0.0f) {
-    int e = __builtin_amdgcn_frexp_expf(f) - 1;
-    emin = min(emin, e);
-    emax = max(emax, e);
-  }
-}
-
-template <int R>
-__global__ void __launch_bounds__(1024)
-rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int K, int logb, int act_bits,
-                       float c_b, uint8_t* __restrict__ codes, float* __restrict__ scales,
-                       uint32_t* __restrict__ precond) {
-  extern __shared__ double xchg[];          // cross-wave butterflies: [R][nthr_pad]
-  __shared__ float red_max[16];
-  __shared__ int red_emin[16], red_emax[16];
-
-  const int tid = threadIdx.x;
-  const int nthr = K / R;
-  const int npad = blockDim.x;
-  const bool active = tid < nthr;
-  const int64_t t = blockIdx.x;
-  const int b = 1 << logb;
-  const int lane = tid & 63, wave = tid >> 6;
-
-  double v[R];
-  load_row<R>(x + t * ldx + (int64_t)tid * R, active, v);
 
   // ---- optional exactness check: exponent spread inside each block ----
   if (precond != nullptr) {
     const int limit = 45 - logb;
-    if (b <= R) {
-      // whole blocks inside this thread
-      for (int s = 0; s < R; s += b) {
-        int emin = 1 << 20, emax = -(1 << 20);
-        for (int i = 0; i < b; ++i) exp_range(v[s + i], emin, emax);
-        if (active && emax >= emin && emax - emin > limit) atomicAdd(precond, 1u);
+    if (b <= 32) {                           // whole blocks inside this thread
+      int emin = 1 << 20, emax = -(1 << 20);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        exp_range(v[i], emin, emax);
+        if (((i + 1) & (b - 1)) == 0) {      // last channel of a block
+          if (active && emax >= emin && emax - emin > limit) atomicAdd(precond, 1u);
+          emin = 1 << 20;
+          emax = -(1 << 20);
+        }
       }
     } else {
       int emin = 1 << 20, emax = -(1 << 20);
 #pragma unroll
-      for (int i = 0; i < R; ++i) exp_range(v[i], emin, emax);
-      const int gth = b / R;                        // threads per block
-      for (int m = 1; m < gth && m < 64; m <<= 1) {
-        emin = min(emin, __shfl_xor(emin, m));
-        emax = max(emax, __shfl_xor(emax, m));
-      }
-      if (gth > 64) {
+      for (int i = 0; i < 32; ++i) exp_range(v[i], emin, emax);
+      const int gth = b >> 5;                // threads per block
+      if (gth > 1) minmax_lanes<1>(emin, emax);
+      if (gth > 2) minmax_lanes<2>(emin, emax);
+      if (gth > 4) minmax_lanes<4>(emin, emax);
+      if (gth > 8) minmax_lanes<8>(emin, emax);
+      if (gth > 16) minmax_lanes<16>(emin, emax);
+      if (gth > 32) minmax_lanes<32>(emin, emax);
+      if (gth > 64) {                        // blocks span waves (G > 64 here)
         if (lane == 0) { red_emin[wave] = emin; red_emax[wave] = emax; }
         __syncthreads();
-        const int wpb = gth / 64;                   // waves per block
+        const int wpb = gth >> 6;            // waves per block
         const int w0 = (wave / wpb) * wpb;
         for (int w = w0; w < w0 + wpb; ++w) {
           emin = min(emin, red_emin[w]);
           emax = max(emax, red_emax[w]);
         }
       }
-      if (active && (tid % gth) == 0 && emax >= emin && emax - emin > limit) atomicAdd(precond, 1u);
+      if (active && (j & (gth - 1)) == 0 && emax >= emin && emax - emin > limit)
+        atomicAdd(precond, 1u);
     }
   }
 
   // ---- fast Walsh-Hadamard transform over blocks of b channels (fp64, exact) ----
 #pragma unroll
-  for (int h = 1; h < R; h <<= 1) {
+  for (int h = 1; h < 32; h <<= 1) {
     if (h < b) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
+      for (int i = 0; i < 32; ++i) {
         if (!(i & h)) {
           const double a = v[i], c = v[i + h];
           v[i] = a + c;
@@ -114,100 +168,114 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int K, int l
       }
     }
   }
-  for (int m = 1; m < 64 && m * R < b; m <<= 1) {
-    const bool upper = (tid & m) != 0;
+  if (b > 32) lane_stage<1>(v, (j & 1) != 0);
+  if (b > 64) lane_stage<2>(v, (j & 2) != 0);
+  if (b > 128) lane_stage<4>(v, (j & 4) != 0);
+  if (b > 256) lane_stage<8>(v, (j & 8) != 0);
+  if (b > 512) lane_stage<16>(v, (j & 16) != 0);
+  if (b > 1024) lane_stage<32>(v, (j & 32) != 0);
+  for (int m = 64; 32 * m < b; m <<= 1) {    // across waves (G > 64 here), 8 values a pass
+    const int npad = blockDim.x;
+    const bool upper = (j & m) != 0;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const double p = __shfl_xor(v[i], m);
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
-    }
-  }
-  for (int m = 64; m * R < b; m <<= 1) {
-    __syncthreads();
+    for (int c = 0; c < 32; c += 8) {
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < R; ++i) xchg[i * npad + tid] = v[i];
-    __syncthreads();
-    const bool upper = (tid & m) != 0;
-    const int partner = tid ^ m;
+      for (int i = 0; i < 8; ++i) xchg[i * npad + tid] = v[c + i];
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const double p = xchg[i * npad + partner];
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
+      for (int i = 0; i < 8; ++i) {
+        const double p = xchg[i * npad + (tid ^ m)];
+        v[c + i] = upper ? (p - v[c + i]) : (v[c + i] + p);
+      }
     }
   }
 
   // ---- per-token absmax ----
-  float u[R];
+  float u[32];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
+  for (int i = 0; i < 32; ++i) {
     u[i] = (float)v[i];                      // round to nearest even
     amax = fmaxf(amax, fabsf(u[i]));
   }
-  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  if (lane == 0) red_max[wave] = amax;
-  __syncthreads();
-  const int nw = npad >> 6;
-  amax = red_max[0];
-  for (int w = 1; w < nw; ++w) amax = fmaxf(amax, red_max[w]);
+  if (G > 1) amax = fmaxf(amax, xor_lane_f32<1>(amax));
+  if (G > 2) amax = fmaxf(amax, xor_lane_f32<2>(amax));
+  if (G > 4) amax = fmaxf(amax, xor_lane_f32<4>(amax));
+  if (G > 8) amax = fmaxf(amax, xor_lane_f32<8>(amax));
+  if (G > 16) amax = fmaxf(amax, xor_lane_f32<16>(amax));
+  if (G > 32) amax = fmaxf(amax, xor_lane_f32<32>(amax));
+  if (G > 64) {
+    if (lane == 0) red_max[wave] = amax;
+    __syncthreads();
+    amax = red_max[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red_max[w]);
+  }
 
-  // ---- quantise: s = M / Q, q = clamp(rint(v / s)) ----
+  // ---- quantise: s = M / Q, q = clamp(rint(fp32(v / s))) ----
   const float Q = act_bits == 4 ? 7.0f : 127.0f;
   const float lo = act_bits == 4 ? -8.0f : -127.0f;
   const float s = amax / Q;
-  int q[R];
+  const double rs = amax > 0.0f ? 1.0 / (double)s : 0.0;
+  int q[32];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    float r = (amax > 0.0f) ? rintf(u[i] / s) : 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    float r = rintf((float)((double)u[i] * rs));
     r = fminf(fmaxf(r, lo), Q);
     q[i] = (int)r;
   }
   if (active) {
     if (act_bits == 4) {
-      uint8_t* dst = codes + t * (K / 2) + (int64_t)tid * (R / 2);
-      uint32_t wds[R / 8];
+      uint32_t w[4];
 #pragma unroll
-      for (int j = 0; j < R / 8; ++j) {
-        uint32_t w = 0;
+      for (int k = 0; k < 4; ++k) {
+        uint32_t d = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w |= ((uint32_t)q[8 * j + i] & 0xFu) << (4 * i);
-        wds[j] = w;
+        for (int i = 0; i < 8; ++i) d |= ((uint32_t)q[8 * k + i] & 0xFu) << (4 * i);
+        w[k] = d;
       }
-      if constexpr (R == 8) *reinterpret_cast<uint32_t*>(dst) = wds[0];
-      else *reinterpret_cast<u32x2*>(dst) = u32x2{wds[0], wds[1]};
+      *reinterpret_cast<u32x4*>(codes + t * (K / 2) + (int64_t)j * 16) = u32x4{w[0], w[1], w[2], w[3]};
     } else {
-      uint8_t* dst = codes + t * K + (int64_t)tid * R;
-      uint32_t wds[R / 4];
+      uint32_t w[8];
 #pragma unroll
-      for (int j = 0; j < R / 4; ++j) {
-        uint32_t w = 0;
+      for (int k = 0; k < 8; ++k) {
+        uint32_t d = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w |= ((uint32_t)q[4 * j + i] & 0xFFu) << (8 * i);
-        wds[j] = w;
+        for (int i = 0; i < 4; ++i) d |= ((uint32_t)q[4 * k + i] & 0xFFu) << (8 * i);
+        w[k] = d;
       }
-      if constexpr (R == 8) *reinterpret_cast<u32x2*>(dst) = u32x2{wds[0], wds[1]};
-      else *reinterpret_cast<u32x4*>(dst) = u32x4{wds[0], wds[1], wds[2], wds[3]};
+      u32x4* dst = reinterpret_cast<u32x4*>(codes + t * K + (int64_t)j * 32);
+      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
     }
+    if (j == 0) scales[t] = amax > 0.0f ? s * c_b : 0.0f;
   }
-  if (tid == 0) scales[t] = (amax > 0.0f) ? s * c_b : 0.0f;
 }
 
 hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t ldx, int b,
                                   int act_bits, uint8_t* codes, float* scales, uint32_t* precond,
                                   hipStream_t stream) {
-  const int R = K <= 8192 ? 8 : 16;
-  const int nthr = K / R;
-  const int npad = (nthr + 63) / 64 * 64;
+  const int nthr = K / 32;
   int logb = 0;
   while ((1 << logb) < b) ++logb;
-  const size_t lds = (b > 64 * R) ? (size_t)npad * R * sizeof(double) : 0;
   const float c_b = (float)(1.0 / std::sqrt((double)b));
-  if (R == 8)
-    hipLaunchKernelGGL(rotate_quantize_kernel<8>, dim3((unsigned)T), dim3(npad), lds, stream, x,
-                       ldx, K, logb, act_bits, c_b, codes, scales, precond);
-  else
-    hipLaunchKernelGGL(rotate_quantize_kernel<16>, dim3((unsigned)T), dim3(npad), lds, stream, x,
-                       ldx, K, logb, act_bits, c_b, codes, scales, precond);
+  int G, threads;
+  int64_t blocks;
+  size_t lds = 0;
+  if (nthr <= 64) {
+    G = 1;
+    while (G < nthr) G <<= 1;
+    threads = 256;
+    const int64_t per_block = 4 * (64 / G);  // tokens per workgroup
+    blocks = (T + per_block - 1) / per_block;
+  } else {
+    G = (nthr + 63) / 64 * 64;
+    threads = G;
+    blocks = T;
+    if (b > 2048) lds = (size_t)threads * 8 * sizeof(double);
+  }
+  hipLaunchKernelGGL(rotate_quantize_kernel, dim3((unsigned)blocks), dim3(threads), lds, stream, x,
+                     ldx, T, K, logb, G, act_bits, c_b, codes, scales, precond);
   return hipGetLastError();
 }
 
