@@ -88,7 +88,9 @@ class MoEPhase:
                        weights=torch.empty((T, k), dtype=torch.float32, device=dev),
                        offsets=torch.empty((E + S + 1,), dtype=torch.int32, device=dev),
                        sorted_tokens=torch.empty((self.R,), dtype=torch.int32, device=dev),
-                       slot_of=torch.empty((T, k), dtype=torch.int32, device=dev))
+                       slot_of=torch.empty((T, k), dtype=torch.int32, device=dev),
+                       ws=torch.empty((max(int(cbq.route_workspace(T, E, k, S)), 1),),
+                                      dtype=torch.uint8, device=dev))
         self.h = torch.empty((self.R, F), dtype=torch.bfloat16, device=dev)
         self.codes_h = torch.empty((self.R, F * a // 8), dtype=torch.uint8, device=dev)
         self.scales_h = torch.empty((self.R,), dtype=torch.float32, device=dev)

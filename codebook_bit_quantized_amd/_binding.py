@@ -138,9 +138,16 @@ def rotate_quantize(x: torch.Tensor, act_bits: int = 4, had_block: int = 0,
     return codes, scales
 
 
+def route_workspace(T: int, E: int, topk: int, n_shared: int = 0) -> int:
+    """Bytes of device workspace moe_route_gather needs (cbq_route_workspace)."""
+    return int(load_library().cbq_route_workspace(T, E, topk, n_shared))
+
+
 def moe_route_gather(logits: torch.Tensor, topk: int, renormalize: bool = True, n_shared: int = 0,
                      out: Optional[dict] = None, stream=None) -> dict:
-    """logits fp32 [T][E] -> dict(ids, weights, offsets, sorted_tokens, slot_of)."""
+    """logits fp32 [T][E] -> dict(ids, weights, offsets, sorted_tokens, slot_of).
+
+    ``out`` may hold preallocated outputs under those names and a workspace under "ws"."""
     lib = load_library()
     _require_gpu(logits)
     T, E = logits.shape
@@ -152,9 +159,13 @@ def moe_route_gather(logits: torch.Tensor, topk: int, renormalize: bool = True, 
     R = T * topk + n_shared * T
     st = o.get("sorted_tokens") if o.get("sorted_tokens") is not None else torch.empty((max(R, 1),), dtype=torch.int32, device=dev)
     so = o.get("slot_of") if o.get("slot_of") is not None else torch.empty((T, topk), dtype=torch.int32, device=dev)
+    need = int(lib.cbq_route_workspace(T, E, topk, n_shared))
+    ws = o.get("ws")
+    if need > 0 and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev)
     _check(lib.cbq_moe_route_gather(_ptr(logits), T, E, topk, int(bool(renormalize)), n_shared,
-                                    _ptr(ids), _ptr(w), _ptr(offs), _ptr(st), _ptr(so), None, 0,
-                                    _stream(stream)))
+                                    _ptr(ids), _ptr(w), _ptr(offs), _ptr(st), _ptr(so),
+                                    _ptr(ws) if need > 0 else None, need, _stream(stream)))
     return dict(ids=ids, weights=w, offsets=offs, sorted_tokens=st[:R], slot_of=so)
 
 

@@ -78,8 +78,9 @@ CBQ_EXPORT int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int6
 }
 
 CBQ_EXPORT size_t cbq_route_workspace(int64_t T, int32_t E, int32_t topk, int32_t n_shared) {
-  (void)T; (void)E; (void)topk; (void)n_shared;
-  return 0;
+  (void)topk; (void)n_shared;
+  if (T <= 0 || E < 1 || E > 256 || T > (1 << 24)) return 0;
+  return cbq::route_workspace_bytes(T, E);
 }
 
 CBQ_EXPORT int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk,
@@ -88,7 +89,6 @@ CBQ_EXPORT int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, i
                                     int32_t* sorted_tokens, int32_t* slot_of, void* ws,
                                     size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  (void)ws; (void)ws_bytes;
   if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
   if (T > (1 << 24)) return fail(CBQ_EUNSUPPORTED, "T must be <= 2^24");
   if (E < 1 || E > 256) return fail(CBQ_EUNSUPPORTED, "E must be in [1, 256] (got %d)", E);
@@ -98,8 +98,13 @@ CBQ_EXPORT int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, i
   if (!expert_offsets) return fail(CBQ_EINVAL, "expert_offsets must be non-null");
   if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_tokens || !slot_of))
     return fail(CBQ_EINVAL, "logits, topk_ids, topk_w, sorted_tokens and slot_of must be non-null");
+  const size_t need = cbq::route_workspace_bytes(T, E);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CBQ_EWORKSPACE, "route workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return fail(CBQ_EINVAL, "ws must be 4-byte aligned");
   hipError_t e = cbq::launch_route(logits, T, E, topk, renormalize, n_shared, topk_ids, topk_w,
-                                   expert_offsets, sorted_tokens, slot_of, (hipStream_t)stream);
+                                   expert_offsets, sorted_tokens, slot_of,
+                                   static_cast<int32_t*>(ws), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_route_gather launch");
   return CBQ_OK;
 }

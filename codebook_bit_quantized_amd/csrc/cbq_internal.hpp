@@ -34,9 +34,10 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
                                   int act_bits, uint8_t* codes, float* scales, uint32_t* precond,
                                   hipStream_t stream);
 
+size_t route_workspace_bytes(int64_t T, int E);
 hipError_t launch_route(const float* logits, int64_t T, int E, int topk, int renormalize,
                         int n_shared, int32_t* ids, float* w, int32_t* offsets,
-                        int32_t* sorted_tokens, int32_t* slot_of, hipStream_t stream);
+                        int32_t* sorted_tokens, int32_t* slot_of, int32_t* ws, hipStream_t stream);
 
 // LUT (decode) path.  max_rows >= 0: experts with more rows are skipped (AUTO split).
 hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream);

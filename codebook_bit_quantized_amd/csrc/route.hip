@@ -30,125 +30,156 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__global__ void __launch_bounds__(256)
+// One wave per token; workgroup c (16 waves) takes the tokens of chunk c and also
+// writes the chunk's per-expert slot counts to ws[c][e] (LDS atomics: the counts do
+// not depend on their order).
+__global__ void __launch_bounds__(1024)
 route_topk_kernel(const float* __restrict__ logits, int64_t T, int E, int topk, int renormalize,
-                  int32_t* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + t * E;
-  constexpr int PER = 4;   // E <= 256
-  uint64_t key[PER];
-  float val[PER];
+                  int chunk, int32_t* __restrict__ ids, float* __restrict__ wts,
+                  int32_t* __restrict__ ws) {
+  __shared__ int s_cnt[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  const int64_t c1 = c0 + chunk < T ? c0 + chunk : T;
+  for (int64_t t = c0 + wave; t < c1; t += 16) {
+    const float* row = logits + t * E;
+    constexpr int PER = 4;   // E <= 256
+    uint64_t key[PER];
+    float val[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    val[i] = e < E ? row[e] : 0.0f;
-    key[i] = e < E ? (((uint64_t)order_bits(val[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e)) : 0ull;
-  }
-  int sel_id[8];
-  float sel_v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= topk) break;
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      val[i] = e < E ? row[e] : 0.0f;
+      key[i] = e < E ? (((uint64_t)order_bits(val[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e)) : 0ull;
     }
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    sel_id[j] = e;
-    sel_v[j] = from_order_bits((uint32_t)(best >> 32));
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i == e) key[i] = 0ull;
-  }
-  const float vmax = sel_v[0];
-  float denom;
-  if (renormalize) {
-    denom = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < topk) denom += expf(sel_v[j] - vmax);
-  } else {
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i < E) part += expf(val[i] - vmax);
-    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
-    denom = part;
-  }
-  if (lane == 0) {
+    int sel_id[8];
+    float sel_v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j < topk) {
-        ids[t * topk + j] = sel_id[j];
-        wts[t * topk + j] = expf(sel_v[j] - vmax) / denom;
+      if (j >= topk) break;
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
+      for (int m = 32; m >= 1; m >>= 1) {
+        const uint64_t o = shfl_xor_u64(best, m);
+        best = o > best ? o : best;
+      }
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+      sel_id[j] = e;
+      sel_v[j] = from_order_bits((uint32_t)(best >> 32));
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (lane + 64 * i == e) key[i] = 0ull;
+    }
+    const float vmax = sel_v[0];
+    float denom;
+    if (renormalize) {
+      denom = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < topk) denom += expf(sel_v[j] - vmax);
+    } else {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (lane + 64 * i < E) part += expf(val[i] - vmax);
+      for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+      denom = part;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < topk) {
+          ids[t * topk + j] = sel_id[j];
+          wts[t * topk + j] = expf(sel_v[j] - vmax) / denom;
+          atomicAdd(&s_cnt[sel_id[j]], 1);
+        }
       }
     }
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) ws[(int64_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-constexpr int SCATTER_CHUNK = 1024;           // tokens per bitmap pass
-constexpr int SCATTER_WORDS = SCATTER_CHUNK / 32;
+constexpr int SCATTER_SUB = 1024;             // tokens per bitmap pass
+constexpr int SCATTER_WORDS = SCATTER_SUB / 32;
 
+// Workgroup c places the slots of chunk c.  An expert's rows start at the rows of all
+// earlier experts plus that expert's slots in earlier chunks (from the counts in
+// ws); inside the chunk a slot's rank is the number of earlier tokens in the
+// expert's token bitmap, so every output is deterministic.
 __global__ void __launch_bounds__(1024)
 route_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int E, int topk, int n_shared,
+                     int chunk, int nchunks, const int32_t* __restrict__ ws,
                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_tokens,
                      int32_t* __restrict__ slot_of) {
-  __shared__ int cnt[256];
+  __shared__ int total[256];
   __shared__ int base[256];
-  __shared__ int chunk_cnt[256];
+  __shared__ int sub_cnt[256];
   __shared__ uint32_t mask[256 * SCATTER_WORDS];
   __shared__ int pre[256 * SCATTER_WORDS];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
+  const int c = blockIdx.x;
   const int64_t nslots = T * topk;
 
-  for (int e = tid; e < E; e += nthr) cnt[e] = 0;
+  for (int e = tid; e < E; e += nthr) {
+    total[e] = 0;
+    base[e] = 0;
+  }
   __syncthreads();
-  for (int64_t i = tid; i < nslots; i += nthr) atomicAdd(&cnt[ids[i]], 1);
+  for (int64_t i = tid; i < (int64_t)nchunks * E; i += nthr) {   // integer sums: order-free
+    const int v = ws[i];
+    const int e = (int)(i % E);
+    atomicAdd(&total[e], v);
+    if (i / E < c) atomicAdd(&base[e], v);
+  }
   __syncthreads();
   if (tid == 0) {
     int run = 0;
     for (int e = 0; e < E; ++e) {
-      base[e] = run;
-      offsets[e] = run;
-      run += cnt[e];
+      base[e] += run;
+      if (c == 0) offsets[e] = run;
+      run += total[e];
     }
-    for (int s = 0; s < n_shared; ++s) {
-      offsets[E + s] = run;
-      run += (int)T;
+    if (c == 0) {
+      for (int s = 0; s < n_shared; ++s) {
+        offsets[E + s] = run;
+        run += (int)T;
+      }
+      offsets[E + n_shared] = run;
     }
-    offsets[E + n_shared] = run;
   }
   __syncthreads();
 
-  for (int64_t c0 = 0; c0 < T; c0 += SCATTER_CHUNK) {
-    const int ct = (int)((T - c0) < SCATTER_CHUNK ? (T - c0) : SCATTER_CHUNK);
-    for (int i = tid; i < E * SCATTER_WORDS; i += nthr) mask[i] = 0u;
+  const int64_t t0 = (int64_t)c * chunk;
+  const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
+  for (int64_t s0 = t0; s0 < t1; s0 += SCATTER_SUB) {
+    const int ct = (int)((t1 - s0) < SCATTER_SUB ? (t1 - s0) : SCATTER_SUB);
+    const int nw = (ct + 31) >> 5;
+    for (int i = tid; i < E * nw; i += nthr) mask[(i / nw) * SCATTER_WORDS + i % nw] = 0u;
     __syncthreads();
     for (int i = tid; i < ct * topk; i += nthr) {
       const int lt = i / topk;
-      const int e = ids[(c0 + lt) * topk + (i - lt * topk)];
+      const int e = ids[(s0 + lt) * topk + (i - lt * topk)];
       atomicOr(&mask[e * SCATTER_WORDS + (lt >> 5)], 1u << (lt & 31));
     }
     __syncthreads();
     for (int e = tid; e < E; e += nthr) {
       int run = 0;
-      for (int w = 0; w < SCATTER_WORDS; ++w) {
+      for (int w = 0; w < nw; ++w) {
         pre[e * SCATTER_WORDS + w] = run;
         run += __popc(mask[e * SCATTER_WORDS + w]);
       }
-      chunk_cnt[e] = run;
+      sub_cnt[e] = run;
     }
     __syncthreads();
     for (int i = tid; i < ct * topk; i += nthr) {
       const int lt = i / topk;
       const int j = i - lt * topk;
-      const int64_t t = c0 + lt;
+      const int64_t t = s0 + lt;
       const int e = ids[t * topk + j];
       const int w = lt >> 5;
       const uint32_t below = mask[e * SCATTER_WORDS + w] & ((1u << (lt & 31)) - 1u);
@@ -157,24 +188,44 @@ route_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int E, int topk
       slot_of[t * topk + j] = row;
     }
     __syncthreads();
-    for (int e = tid; e < E; e += nthr) base[e] += chunk_cnt[e];
+    for (int e = tid; e < E; e += nthr) base[e] += sub_cnt[e];
     __syncthreads();
   }
-  const int64_t nsh = (int64_t)n_shared * T;
-  for (int64_t i = tid; i < nsh; i += nthr) sorted_tokens[nslots + i] = (int32_t)(i % T);
+  // shared experts: row T*k + s*T + t holds token t
+  for (int s = 0; s < n_shared; ++s)
+    for (int64_t t = t0 + tid; t < t1; t += nthr) sorted_tokens[nslots + (int64_t)s * T + t] = (int32_t)t;
+}
+
+// tokens per chunk: at least 16, and at most 256 chunks
+int64_t route_chunk(int64_t T) {
+  int64_t ch = (T + 255) / 256;
+  ch = (ch + 15) / 16 * 16;
+  return ch < 16 ? 16 : ch;
+}
+
+size_t route_workspace_bytes(int64_t T, int E) {
+  if (T <= 0) return 0;
+  const int64_t ch = route_chunk(T);
+  return (size_t)((T + ch - 1) / ch) * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int topk, int renormalize,
                         int n_shared, int32_t* ids, float* w, int32_t* offsets,
-                        int32_t* sorted_tokens, int32_t* slot_of, hipStream_t stream) {
-  if (T > 0) {
-    hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
-                       logits, T, E, topk, renormalize, ids, w);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+                        int32_t* sorted_tokens, int32_t* slot_of, int32_t* ws, hipStream_t stream) {
+  if (T == 0) {
+    // no tokens: every expert range is empty
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(1), dim3(64), 0, stream, ids, T, E, topk,
+                       n_shared, 16, 0, ws, offsets, sorted_tokens, slot_of);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(1), dim3(1024), 0, stream, ids, T, E, topk,
-                     n_shared, offsets, sorted_tokens, slot_of);
+  const int64_t ch = route_chunk(T);
+  const int nch = (int)((T + ch - 1) / ch);
+  hipLaunchKernelGGL(route_topk_kernel, dim3((unsigned)nch), dim3(1024), 0, stream, logits, T, E,
+                     topk, renormalize, (int)ch, ids, w, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)nch), dim3(1024), 0, stream, ids, T, E,
+                     topk, n_shared, (int)ch, nch, ws, offsets, sorted_tokens, slot_of);
   return hipGetLastError();
 }
 

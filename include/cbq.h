@@ -127,8 +127,9 @@ int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
  *                   ascending inside an expert; shared expert s owns rows
  *                   T*topk + s*T + t.
  *  slot_of        : int32 [T][topk]: the row of token t's j-th choice.
- *  ws, ws_bytes   : workspace of at least cbq_route_workspace(...) bytes (may be NULL
- *                   when that is 0).
+ *  ws, ws_bytes   : device workspace of at least cbq_route_workspace(...) bytes, 4-byte
+ *                   aligned (per-chunk expert counts; fully rewritten by every call, so it
+ *                   needs no clearing); may be NULL when that size is 0 (T == 0).
  *  All integer outputs are deterministic (no dependence on atomic ordering).
  *  Requires T <= 2^24.
  */

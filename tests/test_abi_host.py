@@ -68,7 +68,16 @@ def test_route_validation():
     lib = _lib()
     P = _Fake.P
     rg = lib.cbq_moe_route_gather
-    assert lib.cbq_route_workspace(64, 128, 8, 0) == 0
+    # one int32 count per (chunk of >= 16 tokens, expert), at most 256 chunks
+    assert lib.cbq_route_workspace(64, 128, 8, 0) == 4 * 128 * 4
+    assert lib.cbq_route_workspace(4096, 64, 6, 2) == 256 * 64 * 4
+    assert lib.cbq_route_workspace(1 << 20, 256, 8, 0) == 256 * 256 * 4
+    assert lib.cbq_route_workspace(0, 64, 6, 2) == 0
+    W = ctypes.c_void_p(0x7000)
+    assert rg(P, 64, 128, 8, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EWORKSPACE   # no ws
+    assert rg(P, 64, 128, 8, 1, 0, P, P, P, P, P, W, 100, None) == cbq.CBQ_EWORKSPACE    # too small
+    assert rg(P, 64, 128, 8, 1, 0, P, P, P, P, P, ctypes.c_void_p(0x7002), 4096, None) == \
+        cbq.CBQ_EINVAL                                                                 # misaligned
     assert rg(P, 4, 0, 1, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EUNSUPPORTED   # E = 0
     assert rg(P, 4, 300, 1, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EUNSUPPORTED
     assert rg(P, 4, 8, 9, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL          # topk > 8
