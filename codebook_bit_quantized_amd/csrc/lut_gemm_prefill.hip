@@ -178,13 +178,30 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
       const int m0 = ms * 32 + 8 * q + 4 * g;            // rows m0 .. m0+3 of this lane
       const u32x4 ro = *reinterpret_cast<const u32x4*>(&s_rowoff[m0]);
       const f32x4 sc = *reinterpret_cast<const f32x4*>(&s_scale[m0]);
+      if constexpr (NW == 2) {
+        // bf16 h of rows m0..m0+3; lanes nl and nl ^ 1 hold columns 2p and 2p + 1 of
+        // the same rows, so each pair trades one value per two rows and stores whole
+        // dwords: the even lane rows m0 + j, the odd lane rows m0 + j + 1 (j = 0, 2).
+        uint32_t hb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = 4 * q + j;
-        if constexpr (NW == 2) {
+        for (int j = 0; j < 4; ++j) {
+          const int v = 4 * q + j;
           const float gv = acc[ms][0][v] * sc[j], uv = acc[ms][1][v] * sc[j];
-          buf_store_u16(ores, ro[j] + coff[0], f32_to_bf16_rne(silu_mul_fast(gv, uv)));
-        } else {
+          hb[j] = f32_to_bf16_rne(silu_mul_fast(gv, uv));
+        }
+        const bool odd = (nl & 1) != 0;
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const uint32_t send = odd ? hb[j] : hb[j + 1];
+          const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+          const uint32_t word = odd ? (recv | (hb[j + 1] << 16)) : (hb[j] | (recv << 16));
+          const uint32_t off = odd ? ro[j + 1] + coff[0] - 2u : ro[j] + coff[0];
+          __builtin_amdgcn_raw_buffer_store_b32(word, ores, off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = 4 * q + j;
 #pragma unroll
           for (int s = 0; s < 2; ++s) buf_store_f32(ores, ro[j] + coff[s], acc[ms][s][v] * sc[j]);
         }
@@ -208,14 +225,16 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const int tid = threadIdx.x;
   // ---- workgroup -> tile (M-tile ty, column tile tcol) ----
   // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so XCD x
-  // gets ids x, x + 8, ...  In round q those ids take one M-tile of the group
-  // 8q .. 8q + 7, with all its column tiles in a row: the column tiles of one M-tile
-  // read the same activation rows and find them in the same L2.  The XCD of each
-  // slot in the group rotates with q, so an expert's full and partial M-tiles do not
-  // pile up on the same XCDs.  (The host makes the M-tile slots a multiple of 8.)
+  // gets ids x, x + 8, ...; those ids work through rounds of gridDim.x column tiles
+  // of one M-tile each, so the column tiles of an M-tile (same activation rows) share
+  // one L2.  Rounds 2P and 2P + 1 of XCD x take the M-tile pair (2s, 2s + 1),
+  // s = 8P + (x + P) % 8: consecutive M-tiles (usually of one expert: same weights)
+  // stay on one XCD, and the pair slot rotates with P to spread the work.  (The host
+  // makes the M-tile slots a multiple of 16.)
   const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
   const uint32_t q = (lin / 8) / gridDim.x;
-  const int64_t ty = (int64_t)((lin % 8 + q) % 8) + 8 * (int64_t)q;
+  const uint32_t P = q / 2;
+  const int64_t ty = 2 * (8 * (int64_t)P + (lin % 8 + P) % 8) + (q & 1);
   const int tcol = (int)((lin / 8) % gridDim.x);
   // ---- M-tile -> (expert, first row): wave 0 scans the experts' tile counts ----
   if (tid < 64) {
@@ -312,7 +331,7 @@ static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) 
   const int E = a.offsets ? a.E : 1;
   const int ncol = a.n_w == 2 ? 128 : 256;
   int64_t mtiles = (a.n_rows + BM - 1) / BM + (a.offsets ? E : 0);   // M-tile slots
-  mtiles = (mtiles + 7) / 8 * 8;                     // a multiple of 8 (XCD interleave)
+  mtiles = (mtiles + 15) / 16 * 16;                  // a multiple of 16 (XCD pairs)
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2>), grid, dim3(256), 0, stream, a.codes,
