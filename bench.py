@@ -2,18 +2,24 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step is one pass of the whole path (rotate+quantise, route, gate/up GEMM with
-SwiGLU, rotate+quantise of h, down GEMM, combine) over one batch of seeded synthetic
-input.  The default workload is the 64-routed + 2-shared expert layer (hidden 2048,
-FFN 1408, top-6, 3-bit gate/up and 2-bit down codebooks, A4): a 4096-token prefill
-followed by a 32-token decode batch, the one workload that exercises every step of
-the path including both GEMM inner paths.  Inputs are resident in HBM before the
-timed region; the region is bracketed by device synchronisation.
+One step is one pass of the whole path over one batch of seeded synthetic input,
+with inputs resident in HBM before the timed region (bracketed by device
+synchronisation).  For an MoE workload the pass is rotate+quantise, route, gate/up
+GEMM with SwiGLU, rotate+quantise of h, down GEMM and combine for every token batch
+of the workload; for a dense workload it is rotate+quantise and the GEMM of each of
+its two linears for every batch size.
 
-Prints one JSON line: tokens/s over the timed steps, the roofline of the dominant
-kernel (the prefill gate/up GEMM; its duration is measured with HIP events on the
-stream it runs on), the roofline of the decode gate/up GEMM measured separately with
-the caches flushed, and the CPU oracle timed on a bounded sample of the same workload.
+The default workload is the 64-routed + 2-shared expert layer (hidden 2048, FFN 1408,
+top-6, 3-bit gate/up and 2-bit down codebooks, A4): a 4096-token prefill followed by a
+32-token decode batch, the one workload that exercises every step of the path
+including both GEMM inner paths.
+
+Prints one JSON line: tokens/s over the timed steps; the roofline of the dominant
+kernel (the gate/up GEMM of the largest batch: against the fp16 MFMA peak when it
+runs on the MFMA path, with its duration measured by HIP events on its stream inside
+the timed loop; against HBM bandwidth when it runs on the LUT path, measured with the
+caches flushed); the decode gate/up GEMM against HBM for a workload that has both;
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -127,6 +133,49 @@ class MoEPhase:
                                    out=self.h)
 
 
+class DensePhase:
+    """Device buffers and the call sequence for the two decode linears of a dense
+    workload over T tokens: rotate+quantise then GEMM, for 2560 -> 9728 and for
+    9728 -> 2560 (each linear with its own synthetic input)."""
+
+    def __init__(self, cbq, torch, wl, W, xs):
+        self.cbq, self.torch, self.wl, self.W = cbq, torch, wl, W
+        dev = "cuda:0"
+        a = wl.act_bits
+        self.T = xs["gate_up"].shape[0]
+        self.R = self.T
+        self.io = {}
+        for which, x_bits in xs.items():
+            K = x_bits.shape[1]
+            N = W[which].N
+            self.io[which] = dict(
+                x=torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16),
+                codes=torch.empty((self.T, K * a // 8), dtype=torch.uint8, device=dev),
+                scales=torch.empty((self.T,), dtype=torch.float32, device=dev),
+                out=torch.empty((self.T, N), dtype=torch.float32, device=dev))
+        self.path_gu = self.path_dn = cbq.PATH_AUTO
+        self.ev = None
+        self.decode = True
+        self.counts = np.array([self.T])
+
+    def run(self, stream=None):
+        cbq, a = self.cbq, self.wl.act_bits
+        for which in ("gate_up", "down"):
+            b = self.io[which]
+            cbq.rotate_quantize(b["x"], a, codes=b["codes"], scales=b["scales"], stream=stream)
+            if which == "gate_up" and self.ev is not None:
+                self.ev[0].record()
+            cbq.codebook_lut_gemm(b["codes"], b["scales"], a, [self.W[which]], path=cbq.PATH_AUTO,
+                                  out=b["out"], stream=stream)
+            if which == "gate_up" and self.ev is not None:
+                self.ev[1].record()
+
+    def gemm_gu_only(self):
+        b = self.io["gate_up"]
+        self.cbq.codebook_lut_gemm(b["codes"], b["scales"], self.wl.act_bits,
+                                   [self.W["gate_up"]], path=self.cbq.PATH_AUTO, out=b["out"])
+
+
 def choose_path(cbq, counts, routed_E):
     """The path AUTO would give every expert with rows, made explicit so each GEMM is
     one kernel launch (AUTO also launches the other path's grid, which then exits)."""
@@ -145,6 +194,13 @@ def gate_up_bytes(wl, counts, T):
     n_active = int((counts > 0).sum())
     R = int(counts.sum())
     return (2 * per_matrix * n_active + T * (wl.H * wl.act_bits // 8 + 4) + R * 4 + R * wl.F * 2)
+
+
+def dense_gemm_bytes(wl, T):
+    """Algorithmic HBM bytes of the 2560 -> 9728 linear: indices + codebooks once, the
+    token codes and scales once, the fp32 output once."""
+    return (wl.N * wl.K * wl.bits // 8 + wl.N * (1 << wl.bits) * 2 + T * (wl.K * wl.act_bits // 8 + 4)
+            + T * wl.N * 4)
 
 
 def gate_up_flops(wl, counts):
@@ -176,6 +232,30 @@ def cpu_baseline(wl, weights_np, prefill_sample: int, decode_T: int):
                        f"BLAS threads {threads})")
 
 
+def cpu_baseline_dense(wl, weights_np):
+    """Time the oracle on the dense workload's own inputs: rotate+quantise and the
+    dequantise-then-matmul of both linears for every batch size."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    ntok = 0
+    for T in wl.T_list:
+        for which, ws in zip(("gate_up", "down"), weights_np):
+            x = datagen.dense_tokens(wl, T, which)
+            rq = oracle.rotate_quantize(x, 0, wl.act_bits)
+            oracle.expert_gemm(rq["q"].astype(np.int64), rq["scale"], None, None, ws.idx,
+                               ws.codebook, ws.K, ws.bits)
+        ntok += T
+    dt = time.perf_counter() - t0
+    return dict(value=ntok / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"oracle rotate+quantise and both linears for T in {list(wl.T_list)} "
+                       f"({ntok} tokens, {dt:.1f} s, numpy fp64, BLAS threads {threads})")
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -191,8 +271,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(experts would shard across GPUs; see the design notes)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported (a layer "
+              "would shard its experts across GPUs, which is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -216,32 +296,39 @@ def main():
         return
 
     wl = datagen.WORKLOADS[args.workload]
-    if wl.kind != "moe":
-        print("bench.py: the default measurement covers MoE workloads", file=sys.stderr)
-        sys.exit(1)
     t_setup = time.perf_counter()
-    gate_np, up_np, down_np = datagen.moe_weights(wl)
 
     def upw(ws):
         return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
                                    codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
                                    K=ws.K, bits=ws.bits)
 
-    W = dict(gate=upw(gate_np), up=upw(up_np), down=upw(down_np))
-    phases_T = list(wl.T_list)
     phases = []
-    for i, T in enumerate(phases_T):
-        decode = (len(phases_T) == 2 and i == 1)
-        x, lg = datagen.moe_tokens(wl, T, decode=decode)
-        ph = MoEPhase(cbq, torch, wl, W, x, lg, cbq.PATH_AUTO, cbq.PATH_AUTO)
-        ph.run()
+    if wl.kind == "moe":
+        weights_np = datagen.moe_weights(wl)
+        W = dict(gate=upw(weights_np[0]), up=upw(weights_np[1]), down=upw(weights_np[2]))
+        phases_T = list(wl.T_list)
+        for i, T in enumerate(phases_T):
+            decode = (len(phases_T) == 2 and i == 1)
+            x, lg = datagen.moe_tokens(wl, T, decode=decode)
+            ph = MoEPhase(cbq, torch, wl, W, x, lg, cbq.PATH_AUTO, cbq.PATH_AUTO)
+            ph.run()
+            torch.cuda.synchronize()
+            offs = ph.rt["offsets"].cpu().numpy().astype(np.int64)
+            counts = np.diff(offs)
+            ph.counts = counts
+            ph.path_gu = ph.path_dn = choose_path(cbq, counts, wl.E)
+            ph.decode = decode or T <= 64
+            phases.append(ph)
+    else:
+        weights_np = (datagen.dense_weights(wl, "gate_up"), datagen.dense_weights(wl, "down"))
+        W = {"gate_up": upw(weights_np[0]), "down": upw(weights_np[1])}
+        for T in wl.T_list:
+            xs = {w: datagen.dense_tokens(wl, T, w) for w in ("gate_up", "down")}
+            ph = DensePhase(cbq, torch, wl, W, xs)
+            ph.run()
+            phases.append(ph)
         torch.cuda.synchronize()
-        offs = ph.rt["offsets"].cpu().numpy().astype(np.int64)
-        counts = np.diff(offs)
-        ph.counts = counts
-        ph.path_gu = ph.path_dn = choose_path(cbq, counts, wl.E)
-        ph.decode = decode or T <= 64
-        phases.append(ph)
     setup_s = time.perf_counter() - t_setup
 
     # dominant kernel: the gate/up GEMM of the largest phase
@@ -269,21 +356,10 @@ def main():
     value = tokens / (ms_per_step / 1000.0)
     dom_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(start_evs, end_evs)]))
 
-    dom_flops = gate_up_flops(wl, dom.counts)
-    achieved = dom_flops / (dom_ms / 1000.0) / 1e12
-    kernel = "mfma_prefill" if dom.path_gu == cbq.PATH_MFMA else "lut_decode"
-    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=F16_MFMA_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / F16_MFMA_PEAK_TFLOPS, 4),
-                    traffic=read_traffic(kernel, wl.name),
-                    kernel=f"{kernel} gate/up+SwiGLU", avg_launch_us=round(dom_ms * 1000.0, 2),
-                    algorithmic_flops=dom_flops)
-
-    # decode gate/up GEMM roofline, cold caches (flush > MALL between reps)
-    decode_info = None
-    dec = [p for p in phases if p.decode and p is not dom]
-    if dec:
-        p = dec[0]
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    def cold_gemm_ms(p):
+        """Median duration of p's gate/up GEMM with the caches flushed (1 GiB written,
+        more than L2 + MALL) before every repetition."""
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         times = []
         for _ in range(args.decode_reps):
             flush.fill_(1.0)
@@ -294,25 +370,61 @@ def main():
             torch.cuda.synchronize()
             times.append(s.elapsed_time(e))
         del flush
-        d_ms = float(np.median(times))
-        d_bytes = gate_up_bytes(wl, p.counts, p.T)
+        return float(np.median(times))
+
+    def hbm_roofline(p, label):
+        d_ms = cold_gemm_ms(p)
+        if wl.kind == "moe":
+            d_bytes = gate_up_bytes(wl, p.counts, p.T)
+            extra = dict(active_experts=int((p.counts > 0).sum()))
+        else:
+            d_bytes = dense_gemm_bytes(wl, p.T)
+            extra = {}
         gbs = d_bytes / (d_ms / 1000.0) / 1e9
-        decode_info = dict(tokens=p.T, bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
-                           unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                           traffic=read_traffic("lut_decode", wl.name),
-                           kernel="lut_decode gate/up+SwiGLU (caches flushed)",
-                           median_launch_us=round(d_ms * 1000.0, 2), algorithmic_bytes=d_bytes,
-                           active_experts=int((p.counts > 0).sum()))
+        return dict(tokens=p.T, bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                    traffic=read_traffic("lut_decode", wl.name), kernel=label,
+                    avg_launch_us=round(d_ms * 1000.0, 2), algorithmic_bytes=d_bytes, **extra)
+
+    decode_info = None
+    if wl.kind == "moe" and dom.path_gu == cbq.PATH_MFMA:
+        dom_flops = gate_up_flops(wl, dom.counts)
+        achieved = dom_flops / (dom_ms / 1000.0) / 1e12
+        roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=F16_MFMA_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(achieved / F16_MFMA_PEAK_TFLOPS, 4),
+                        traffic=read_traffic("mfma_prefill", wl.name),
+                        kernel="mfma_prefill gate/up+SwiGLU", avg_launch_us=round(dom_ms * 1000.0, 2),
+                        algorithmic_flops=dom_flops)
+        # the decode gate/up GEMM, cold caches
+        dec = [p for p in phases if p.decode and p is not dom]
+        if dec:
+            decode_info = hbm_roofline(dec[0], "lut_decode gate/up+SwiGLU (caches flushed)")
+            decode_info["median_launch_us"] = decode_info.pop("avg_launch_us")
+    else:
+        # every phase is decode-sized: the dominant GEMM is HBM-bound; its roofline is
+        # taken with cold caches (the in-loop launches may hit the MALL)
+        label = ("lut_decode gate/up+SwiGLU" if wl.kind == "moe" else
+                 f"lut_decode {wl.K}->{wl.N} linear") + " (caches flushed)"
+        roofline = hbm_roofline(dom, label)
+        roofline["in_loop_avg_launch_us"] = round(dom_ms * 1000.0, 2)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, (gate_np, up_np, down_np), args.cpu_prefill_sample,
-                           phases_T[1] if len(phases_T) > 1 else 32)
+        if wl.kind == "moe":
+            cpu = cpu_baseline(wl, weights_np, args.cpu_prefill_sample,
+                               wl.T_list[1] if len(wl.T_list) > 1 else 32)
+        else:
+            cpu = cpu_baseline_dense(wl, weights_np)
 
-    cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
-               hidden=wl.H, ffn=wl.F, experts=wl.E, shared_experts=wl.n_shared, topk=wl.topk,
-               bits_gate_up=wl.bits_gate_up, bits_down=wl.bits_down, act_bits=wl.act_bits,
-               paths={str(p.T): int(p.path_gu) for p in phases})
+    if wl.kind == "moe":
+        cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
+                   hidden=wl.H, ffn=wl.F, experts=wl.E, shared_experts=wl.n_shared, topk=wl.topk,
+                   bits_gate_up=wl.bits_gate_up, bits_down=wl.bits_down, act_bits=wl.act_bits,
+                   paths={str(p.T): int(p.path_gu) for p in phases})
+    else:
+        cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
+                   linears=[f"{wl.K}->{wl.N}", f"{wl.N}->{wl.K}"], bits=wl.bits,
+                   act_bits=wl.act_bits, paths={str(p.T): int(p.path_gu) for p in phases})
     line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,
