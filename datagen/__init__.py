@@ -43,6 +43,7 @@ TAG_UP_IDX = 12
 TAG_UP_CB = 13
 TAG_DOWN_IDX = 14
 TAG_DOWN_CB = 15
+TAG_W_FULL = 16        # full-precision weights (input of codebook construction)
 TAG_MISC = 99
 
 OUTLIER_CHANNELS = (3, 77)
@@ -131,6 +132,15 @@ def indices_u8(workload_id: int, tag: int, expert: int, N: int, K: int, bits: in
     out = (v % L).astype(np.uint8)
     out[v < L] = L
     return out
+
+
+def weights_bf16(workload_id: int, tag: int, expert: int, N: int, K: int) -> np.ndarray:
+    """bf16 bit patterns [N][K] of full-precision weights: N(0, 0.02) draws with one
+    entry in 256 scaled by 8 (weight outliers)."""
+    g = rng_for(workload_id, tag, expert)
+    w = g.standard_normal((N, K), dtype=np.float32) * np.float32(CODEBOOK_SIGMA)
+    w[g.random((N, K)) < 1.0 / 256.0] *= np.float32(8.0)
+    return f32_to_bf16_bits(w)
 
 
 # ---------------------------------------------------------------------------

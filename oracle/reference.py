@@ -51,7 +51,8 @@ __all__ = [
     "quantize", "rotate_quantize", "pack_codes", "unpack_codes", "unpack_indices",
     "dequantize", "expert_gemm", "dense_gemm", "gemm_entry", "lut_gemm_table",
     "lut_gemm_buckets", "route", "silu_mul_bf16", "round_f64_to_bf16_bits", "combine",
-    "moe_layer", "ACT_LEVELS",
+    "moe_layer", "ACT_LEVELS", "bf16_order_keys", "round_f64_to_f16_bits",
+    "kmeans_precondition", "kmeans_row", "kmeans_codebooks",
 ]
 
 # quantiser parameters per activation width: (Q, lower clamp, upper clamp)
@@ -431,3 +432,88 @@ def moe_layer(x_bits: np.ndarray, logits: np.ndarray, gate, up, down, topk: int,
     out_in = out if down_override is None else down_override
     y = combine(out_in, rt["slot_of"], rt["weights"], T, topk, n_shared)
     return dict(rq=rq, route=rt, gate=g, up=u, h=h_bits, rqh=rqh, out=out, y=y)
+
+
+# ---------------------------------------------------------------------------
+# Offline codebook construction (CodeQuant2 Figure 3 right: K-means initialises the
+# centroid matrix and the per-row assignments; CodeQuant abstract: weight outliers are
+# absorbed into cluster centroids).  One 1-D K-means per weight row.
+def bf16_order_keys(bits: np.ndarray) -> np.ndarray:
+    """uint16 keys that sort bf16 patterns in numeric order (-0 just before +0)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return np.where(b & 0x8000, (~b) & 0xFFFF, b | 0x8000).astype(np.uint16)
+
+
+def round_f64_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp64 once to fp16 (nearest, ties to even, subnormals kept, overflow to
+    inf); uint16 patterns.  Written out on the fp16 grid so that no intermediate
+    format rounds first."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    q = np.maximum(ex.astype(np.int64) - 1, -14) - 10        # fp16 spacing at |x|
+    m = np.rint(np.ldexp(a, -q))                              # exact scaling, RNE
+    y = np.ldexp(m, q)
+    with np.errstate(over="ignore"):
+        h = np.where(y >= 65520.0, np.inf, y).astype(np.float16)   # exact or inf
+    h = np.where(np.signbit(x), -h, h).astype(np.float16)
+    return h.view(np.uint16)
+
+
+def kmeans_precondition(w_bits: np.ndarray) -> bool:
+    """True when fp64 sums of any subset of the row are exact (same bound as the
+    rotation: nonzero exponents spread at most 45 - ceil(log2 K) binades)."""
+    w = bf16_bits_to_f64(w_bits)
+    K = w.shape[-1]
+    return bool(rotation_precondition(w[None, :], 1 << max(0, (K - 1).bit_length()))[0])
+
+
+def kmeans_row(w_bits: np.ndarray, bits: int, max_iters: int, return_f64: bool = False):
+    """Lloyd's K-means of one bf16 row into L = 2^bits clusters.
+
+    * init: sort the row (by value; -0 before +0) and take the values at ranks
+      floor((2j + 1) K / (2L)), j = 0..L-1;
+    * each round: assign every weight to the centroid at the smallest |w - c| (fp64,
+      ties to the lower index); stop if no assignment changed since the last round;
+      otherwise every non-empty cluster's centroid becomes the mean of its weights
+      (exact fp64 sum / count, one IEEE division); at most max_iters updates;
+    * output: centroids rounded once to fp16, then a final assignment against the
+      fp16 values (same rule).
+    Returns (indices [K] int64, codebook fp16 bits [L], number of updates), plus the
+    fp64 centroids before rounding when return_f64."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    w = bf16_bits_to_f64(w_bits)
+    K, L = w.shape[0], 1 << bits
+    order = np.argsort(bf16_order_keys(w_bits), kind="stable")
+    ranks = ((2 * np.arange(L) + 1) * K) // (2 * L)
+    c = w[order][ranks].copy()
+    prev = None
+    updates = 0
+    for _ in range(max_iters):
+        a = np.argmin(np.abs(w[:, None] - c[None, :]), axis=1)   # first minimum: lower index
+        if prev is not None and np.array_equal(a, prev):
+            break
+        for j in range(L):
+            m = a == j
+            n = int(m.sum())
+            if n:
+                c[j] = math.fsum(w[m]) / n
+        prev = a
+        updates += 1
+    cb = round_f64_to_f16_bits(c)
+    a = np.argmin(np.abs(w[:, None] - f16_bits_to_f64(cb)[None, :]), axis=1)
+    if return_f64:
+        return a.astype(np.int64), cb, updates, c
+    return a.astype(np.int64), cb, updates
+
+
+def kmeans_codebooks(w_bits: np.ndarray, bits: int, max_iters: int):
+    """kmeans_row over every row of w_bits [R][K]: (indices [R][K], codebooks [R][L],
+    updates [R])."""
+    R = w_bits.shape[0]
+    idx = np.empty(w_bits.shape, dtype=np.int64)
+    cb = np.empty((R, 1 << bits), dtype=np.uint16)
+    it = np.empty(R, dtype=np.int64)
+    for r in range(R):
+        idx[r], cb[r], it[r] = kmeans_row(w_bits[r], bits, max_iters)
+    return idx, cb, it
