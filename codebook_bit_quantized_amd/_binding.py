@@ -25,7 +25,7 @@ AUTO_MAX_LUT_ROWS = 32
 # every symbol include/cbq.h declares
 EXPORTED = ("cbq_rotate_quantize", "cbq_route_workspace", "cbq_moe_route_gather",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
-            "cbq_status_string", "cbq_last_error", "cbq_version")
+            "cbq_kmeans_codebooks", "cbq_status_string", "cbq_last_error", "cbq_version")
 
 
 class CbqError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cbq_codebook_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, vp, vp, W, i32, i32, i32, vp,
                                                  i64, vp, sz, vp]),
         "cbq_moe_combine": (ctypes.c_int, [vp, vp, vp, i64, i32, i32, i32, vp, vp]),
+        "cbq_kmeans_codebooks": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
         "cbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "cbq_last_error": (ctypes.c_char_p, []),
         "cbq_version": (ctypes.c_int, []),
@@ -204,6 +205,26 @@ def moe_combine(expert_out: torch.Tensor, slot_of: torch.Tensor, topk_w: torch.T
     _check(lib.cbq_moe_combine(_ptr(expert_out), _ptr(slot_of), _ptr(topk_w), T, topk, H, n_shared,
                                _ptr(y), _stream(stream)))
     return y
+
+
+def kmeans_codebooks(w: torch.Tensor, bits: int, max_iters: int = 50, idx: Optional[torch.Tensor] = None,
+                     codebook: Optional[torch.Tensor] = None, iters_done: Optional[torch.Tensor] = None,
+                     stream=None) -> CodebookWeights:
+    """bf16 weight rows [R][K] (last dim contiguous) -> CodebookWeights (E = 1, N = R): one
+    K-means per row (cbq_kmeans_codebooks)."""
+    lib = load_library()
+    _require_gpu(w)
+    R, K = w.shape
+    if w.stride(1) != 1:
+        raise ValueError("w rows must be contiguous")
+    dev = w.device
+    if idx is None:
+        idx = torch.empty((1, R, K * bits // 8), dtype=torch.uint8, device=dev)
+    if codebook is None:
+        codebook = torch.empty((1, R, 1 << bits), dtype=torch.int16, device=dev)
+    _check(lib.cbq_kmeans_codebooks(_ptr(w), R, K, w.stride(0), bits, max_iters, _ptr(idx),
+                                    _ptr(codebook), _ptr(iters_done), _stream(stream)))
+    return CodebookWeights(idx=idx, codebook=codebook, K=K, bits=bits)
 
 
 def moe_ffn(x: torch.Tensor, logits: torch.Tensor, gate: CodebookWeights, up: CodebookWeights,

@@ -178,6 +178,28 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   return CBQ_OK;
 }
 
+CBQ_EXPORT int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw,
+                                    int32_t bits, int32_t max_iters, uint8_t* idx,
+                                    uint16_t* codebook, int32_t* iters_done, void* stream) {
+  g_err[0] = 0;
+  if (R < 0) return fail(CBQ_EINVAL, "R must be >= 0 (got %lld)", (long long)R);
+  if (R > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "R must be < 2^31");
+  if (K < 32 || K % 32) return fail(CBQ_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (K > 16384) return fail(CBQ_EUNSUPPORTED, "K must be <= 16384 (got %d)", K);
+  if (ldw < K) return fail(CBQ_EINVAL, "ldw must be >= K (got %lld)", (long long)ldw);
+  if (bits < 2 || bits > 4) return fail(CBQ_EUNSUPPORTED, "bits must be 2, 3 or 4 (got %d)", bits);
+  if (max_iters < 0 || max_iters > 1000) return fail(CBQ_EINVAL, "max_iters must be in [0, 1000]");
+  if (R == 0) return CBQ_OK;
+  if (!w || !idx || !codebook) return fail(CBQ_EINVAL, "w, idx and codebook must be non-null");
+  if ((reinterpret_cast<uintptr_t>(idx) & 3u) || (reinterpret_cast<uintptr_t>(w) & 1u) ||
+      (reinterpret_cast<uintptr_t>(codebook) & 1u))
+    return fail(CBQ_EINVAL, "idx must be 4-byte aligned, w and codebook 2-byte aligned");
+  hipError_t e = cbq::launch_kmeans(w, R, K, ldw, bits, max_iters, idx, codebook, iters_done,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kmeans_codebooks launch");
+  return CBQ_OK;
+}
+
 CBQ_EXPORT int cbq_moe_combine(const float* expert_out, const int32_t* slot_of, const float* topk_w,
                                int64_t T, int32_t topk, int32_t H, int32_t n_shared, float* y,
                                void* stream) {

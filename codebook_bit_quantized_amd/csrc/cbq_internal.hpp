@@ -45,6 +45,10 @@ hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream
 // MFMA (prefill) path.  Experts with at most min_rows rows are skipped (AUTO split).
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream);
 
+hipError_t launch_kmeans(const uint16_t* w, int64_t R, int K, int64_t ldw, int bits, int max_iters,
+                         uint8_t* idx, uint16_t* codebook, int32_t* iters_done,
+                         hipStream_t stream);
+
 hipError_t launch_combine(const float* expert_out, const int32_t* slot_of, const float* w,
                           int64_t T, int topk, int H, int n_shared, float* y, hipStream_t stream);
 

@@ -189,6 +189,34 @@ int cbq_moe_combine(const float* expert_out, const int32_t* slot_of, const float
                     int64_t T, int32_t topk, int32_t H, int32_t n_shared, float* y,
                     void* stream);
 
+/*
+ * cbq_kmeans_codebooks - offline codebook construction, one 1-D K-means per weight row.
+ * Passage: CodeQuant2, Figure 3 (right: K-means initialises the centroid matrix and the
+ * per-row assignment matrices); CodeQuant abstract (weight outliers absorbed into
+ * cluster centroids).
+ *
+ *  w          : bf16 [R][ldw] weight rows (ldw >= K); row r is clustered on its own.
+ *  bits       : 2, 3 or 4: L = 2^bits clusters per row.
+ *  max_iters  : 0 .. 1000 centroid updates at most.
+ *  idx        : [R][K*bits/8] bytes, 4-byte aligned: the assignments as the LSB-first
+ *               bitstream cbq_weights uses.
+ *  codebook   : fp16 [R][L]: the centroids.
+ *  iters_done : optional int32 [R]: the number of updates made per row.
+ *
+ *  Per row: sort the values (-0 before +0); initial centroids are the values at
+ *  ranks floor((2j + 1) K / (2L)); each round assigns every weight to the centroid
+ *  with the smallest fp64 |w - c| (ties to the lower index) and stops if no
+ *  assignment changed, else replaces every non-empty cluster's centroid by its mean
+ *  (fp64 sum / count, one division).  The centroids are then rounded once to fp16
+ *  and the weights are assigned against those fp16 values.  The sums are exact (so
+ *  the result is deterministic) for rows whose nonzero exponents spread at most
+ *  45 - ceil(log2 K) binades.  Requires K % 32 == 0, 32 <= K <= 16384.
+ *  The output (idx, codebook, E = 1, N = R) is a ready cbq_weights set.
+ */
+int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw, int32_t bits,
+                         int32_t max_iters, uint8_t* idx, uint16_t* codebook,
+                         int32_t* iters_done, void* stream);
+
 /* Name of a status code, and the calling thread's message for its last failure. */
 const char* cbq_status_string(int status);
 const char* cbq_last_error(void);
