@@ -256,6 +256,55 @@ def cpu_baseline_dense(wl, weights_np):
                        f"({ntok} tokens, {dt:.1f} s, numpy fp64, BLAS threads {threads})")
 
 
+def bench_kmeans(args, cbq, torch):
+    """Codebook construction for every gate matrix of the workload (E + S experts x F rows
+    of H bf16 weights, 2^bits_gate_up clusters): rows/s, against the time to stream the
+    rows in and the codebooks out at HBM bandwidth (the kernel is bound by its
+    sort and its dependent search steps, well short of that)."""
+    import oracle
+    wl = datagen.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    R, K, bits = (wl.E + wl.n_shared) * wl.F, wl.H, wl.bits_gate_up
+    max_iters = 50
+    w_np = datagen.weights_bf16(wl.wid, datagen.TAG_W_FULL, 0, R, K)
+    w = torch.from_numpy(w_np.view(np.int16)).to(dev)
+    it = torch.empty((R,), dtype=torch.int32, device=dev)
+    cw = cbq.kmeans_codebooks(w, bits, max_iters, iters_done=it)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, args.steps // 4)):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        cbq.kmeans_codebooks(w, bits, max_iters, idx=cw.idx, codebook=cw.codebook, iters_done=it)
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) / 1000.0)
+    t = float(np.median(times))
+    rounds = it.cpu().numpy().astype(np.int64) + 1          # the last round finds no change
+    # streaming bound: the bf16 rows in, the packed indices and fp16 codebooks out
+    nbytes = R * K * 2 + R * K * bits // 8 + R * (1 << bits) * 2
+    gbs = nbytes / t / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = 64
+        t0 = time.perf_counter()
+        oracle.kmeans_codebooks(w_np[:n], bits, max_iters)
+        dt = time.perf_counter() - t0
+        cpu = dict(value=n / dt, unit="rows/s", cores=1, kind="oracle",
+                   sample=f"oracle per-row K-means on the first {n} rows ({dt:.1f} s, numpy fp64)")
+    line = dict(metric="codebook construction rows/s", value=round(R / t, 1), unit="rows/s",
+                n_gpus=1, steps=len(times), warmup=1, ms_per_step=round(t * 1000.0, 3),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f64",
+                data="synthetic",
+                config=dict(workload=f"kmeans_gate_{wl.name}", rows=R, K=K, bits=bits,
+                            max_iters=max_iters, mean_rounds=round(float(rounds.mean()), 2)),
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                              kernel="kmeans_rows", algorithmic_bytes=nbytes),
+                cpu_baseline=cpu, host=platform.node())
+    print(json.dumps(line))
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -266,6 +315,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefill-sample", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--kmeans", action="store_true",
+                    help="measure offline codebook construction (per-row K-means) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -293,6 +344,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+        return
+
+    if args.kmeans:
+        bench_kmeans(args, cbq, torch)
         return
 
     wl = datagen.WORKLOADS[args.workload]

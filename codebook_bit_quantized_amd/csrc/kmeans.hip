@@ -5,15 +5,18 @@
 // cluster centroids.  The output is exactly the format the LUT GEMM consumes: per
 // row a 2^bits-entry fp16 codebook and an LSB-first bitstream of indices.
 //
-// One wave per row.  The row's bf16 patterns are sorted in LDS (bitonic network on
-// order-preserving 16-bit keys, padded to a power of two with keys that sort last);
+// One wave per row.  The row's bf16 patterns are sorted (bitonic network on
+// order-preserving 16-bit keys, padded to a power of two with keys that sort last; in
+// registers for rows up to 2048 channels, in LDS beyond);
 // the initial centroids are the values at ranks floor((2j + 1) K / (2L)).  Each
 // Lloyd round assigns every weight to the nearest centroid (fp64 |w - c|, ties to
 // the lower index), sums the clusters in fp64 (exact for a row whose nonzero
 // exponents spread at most 45 - ceil(log2 K) binades, so the order of the sums does
 // not matter) and divides once.  In one dimension the clusters of the sorted row
-// are contiguous ranges, so the assignment is unchanged exactly when every cluster
-// count is; the rounds stop then, or after max_iters updates.  The centroids are
+// are contiguous ranges: each round finds the range boundaries by binary search and
+// takes the cluster sums from exact prefix sums of the sorted row, and the
+// assignment is unchanged exactly when every cluster count is; the rounds stop
+// then, or after max_iters updates.  The centroids are
 // rounded once to fp16 and the weights, in their original order, are assigned
 // against the fp16 values.
 #include "cbq_internal.hpp"
@@ -80,67 +83,160 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 
 }  // namespace
 
-template <int BITS>
+// Bitonic sort of Kp = 64 * KPL keys held KPL per lane (element i = lane * KPL + r):
+// exchanges closer than KPL stay in a lane's registers, wider ones pair lanes.
+template <int KPL>
+__device__ __forceinline__ void sort_in_registers(uint32_t (&v)[KPL], int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64 * KPL; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < KPL) {
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          const int rp = r ^ j;
+          if (rp > r) {
+            const bool up = (((lane * KPL + r) & k) == 0);
+            const uint32_t a = v[r], b = v[rp];
+            const uint32_t lo = a < b ? a : b, hi = a < b ? b : a;
+            v[r] = up ? lo : hi;
+            v[rp] = up ? hi : lo;
+          }
+        }
+      } else {
+        const int m = j / KPL;                     // partner lane = lane ^ m
+        const bool lower = (lane & m) == 0;
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          const bool up = (((lane * KPL + r) & k) == 0);
+          const uint32_t p = (uint32_t)__shfl_xor((int)v[r], m);
+          const uint32_t lo = v[r] < p ? v[r] : p, hi = v[r] < p ? p : v[r];
+          v[r] = (lower == up) ? lo : hi;
+        }
+      }
+    }
+  }
+}
+
+template <int BITS, int KPL>
 __global__ void __launch_bounds__(64)
-kmeans_rows_kernel(const uint16_t* __restrict__ w, int64_t ldw, int K, int Kp, int max_iters,
-                   uint8_t* __restrict__ idx, uint16_t* __restrict__ codebook,
+kmeans_rows_kernel(const uint16_t* __restrict__ w, int64_t ldw, int K, int Kp, int use_prefix,
+                   int max_iters, uint8_t* __restrict__ idx, uint16_t* __restrict__ codebook,
                    int32_t* __restrict__ iters_done) {
   constexpr int L = 1 << BITS;
-  extern __shared__ uint16_t keys[];               // [Kp]
+  extern __shared__ __attribute__((aligned(16))) uint16_t keys[];   // [Kp], then fp64 P[K + 1]
+  double* P = reinterpret_cast<double*>(keys + ((Kp + 3) & ~3));
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint16_t* src = w + row * ldw;
 
   // ---- sort the row's keys ----
-  for (int i = lane; i < Kp; i += 64) keys[i] = i < K ? (uint16_t)order_key16(src[i]) : (uint16_t)0xFFFFu;
-  __syncthreads();
-  for (int k = 2; k <= Kp; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = lane; i < Kp; i += 64) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint16_t a = keys[i], b = keys[l];
-          const bool up = (i & k) == 0;
-          if (up ? (a > b) : (a < b)) { keys[i] = b; keys[l] = a; }
-        }
-      }
-      __syncthreads();
+  if constexpr (KPL > 0) {                         // Kp == 64 * KPL: in registers
+    uint32_t v[KPL];
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      const int i = lane * KPL + r;
+      v[r] = i < K ? order_key16(src[i]) : 0xFFFFu;
     }
+    sort_in_registers<KPL>(v, lane);
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) keys[lane * KPL + r] = (uint16_t)v[r];
+    __syncthreads();
+  } else {                                         // longer rows: the network in LDS
+    for (int i = lane; i < Kp; i += 64) keys[i] = i < K ? (uint16_t)order_key16(src[i]) : (uint16_t)0xFFFFu;
+    __syncthreads();
+    for (int k = 2; k <= Kp; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = lane; i < Kp; i += 64) {
+          const int l = i ^ j;
+          if (l > i) {
+            const uint16_t a = keys[i], b = keys[l];
+            const bool up = (i & k) == 0;
+            if (up ? (a > b) : (a < b)) { keys[i] = b; keys[l] = a; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  auto value = [&](int i) { return bf16_bits_to_f64(key16_to_bits(keys[i])); };
+
+  // ---- prefix sums of the sorted row (exact): P[i] = sum of the i smallest ----
+  if (use_prefix) {
+    const int seg = (K + 63) / 64;
+    const int i0 = min(lane * seg, K), i1 = min(i0 + seg, K);
+    double run = 0.0;
+    for (int i = i0; i < i1; ++i) run += value(i);
+    double incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    double acc = incl - run;                       // exact: a representable partial sum
+    if (lane == 0) P[0] = 0.0;
+    for (int i = i0; i < i1; ++i) {
+      acc += value(i);
+      P[i + 1] = acc;
+    }
+    __syncthreads();
   }
 
   // ---- initial centroids: values at ranks floor((2j + 1) K / (2L)) ----
   double c[L];
 #pragma unroll
-  for (int j = 0; j < L; ++j) c[j] = bf16_bits_to_f64(key16_to_bits(keys[((2 * j + 1) * K) / (2 * L)]));
+  for (int j = 0; j < L; ++j) c[j] = value(((2 * j + 1) * K) / (2 * L));
 
   // ---- Lloyd rounds over the sorted row ----
+  // The nearest-centroid index is non-decreasing along the sorted row (for ordered
+  // centroids and monotone rounding), so cluster j is the range [b_j, b_{j+1}) with
+  // b_j the first position whose nearest centroid is >= j: one binary search per
+  // boundary instead of a pass over the row.
   int prev[L];
 #pragma unroll
   for (int j = 0; j < L; ++j) prev[j] = -1;
   int updates = 0;
   for (int it = 0; it < max_iters; ++it) {
-    double s[L];
-    int n[L];
-#pragma unroll
-    for (int j = 0; j < L; ++j) { s[j] = 0.0; n[j] = 0; }
-    for (int i = lane; i < K; i += 64) {
-      const double v = bf16_bits_to_f64(key16_to_bits(keys[i]));
-      const int a = nearest<L>(v, c);
-#pragma unroll
-      for (int j = 0; j < L; ++j) {
-        if (a == j) { s[j] += v; n[j] += 1; }
+    int bnd = K;                                   // lane j: boundary b_{j+1}
+    if (lane < L - 1) {
+      int lo = 0, hi = K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (nearest<L>(value(mid), c) >= lane + 1) hi = mid; else lo = mid + 1;
       }
+      bnd = lo;
     }
+    int b[L + 1];
+    b[0] = 0;
+    b[L] = K;
+#pragma unroll
+    for (int j = 1; j < L; ++j) b[j] = __shfl(bnd, j - 1);
+    int n[L];
     bool same = true;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-      n[j] = wave_sum_i32(n[j]);
+      n[j] = b[j + 1] - b[j];
       same = same && (n[j] == prev[j]);
     }
     if (same) break;                               // counts fix the contiguous clusters
+    double s[L];
+    if (use_prefix) {
+#pragma unroll
+      for (int j = 0; j < L; ++j) s[j] = P[b[j + 1]] - P[b[j]];   // exact difference
+    } else {
+#pragma unroll
+      for (int j = 0; j < L; ++j) s[j] = 0.0;
+      for (int i = lane; i < K; i += 64) {
+        const double v = value(i);
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+          if (i >= b[j] && i < b[j + 1]) s[j] += v;
+      }
+#pragma unroll
+      for (int j = 0; j < L; ++j) s[j] = wave_sum_f64(s[j]);
+    }
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-      s[j] = wave_sum_f64(s[j]);
       if (n[j] > 0) c[j] = s[j] / (double)n[j];
       prev[j] = n[j];
     }
@@ -181,20 +277,45 @@ kmeans_rows_kernel(const uint16_t* __restrict__ w, int64_t ldw, int K, int Kp, i
   }
 }
 
+template <int B, int KPL>
+static void launch_one(dim3 grid, size_t lds, hipStream_t stream, const uint16_t* w, int64_t ldw,
+                       int K, int Kp, int use_prefix, int max_iters, uint8_t* idx,
+                       uint16_t* codebook, int32_t* iters_done) {
+  hipLaunchKernelGGL((kmeans_rows_kernel<B, KPL>), grid, dim3(64), lds, stream, w, ldw, K, Kp,
+                     use_prefix, max_iters, idx, codebook, iters_done);
+}
+
+template <int B>
+static void launch_bits(int kpl, dim3 grid, size_t lds, hipStream_t stream, const uint16_t* w,
+                        int64_t ldw, int K, int Kp, int use_prefix, int max_iters, uint8_t* idx,
+                        uint16_t* codebook, int32_t* iters_done) {
+  switch (kpl) {
+    case 1: launch_one<B, 1>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 2: launch_one<B, 2>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 4: launch_one<B, 4>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 8: launch_one<B, 8>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 16: launch_one<B, 16>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 32: launch_one<B, 32>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    default: launch_one<B, 0>(grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+  }
+}
+
 hipError_t launch_kmeans(const uint16_t* w, int64_t R, int K, int64_t ldw, int bits, int max_iters,
                          uint8_t* idx, uint16_t* codebook, int32_t* iters_done,
                          hipStream_t stream) {
   int Kp = 1;
   while (Kp < K) Kp <<= 1;
-  const size_t lds = (size_t)Kp * sizeof(uint16_t);
-  const dim3 grid((unsigned)R), block(64);
+  // prefix sums of the sorted row in LDS up to 8192 channels (80 KB); longer rows sum
+  // each cluster range in a pass over the row
+  const int use_prefix = K <= 8192;
+  const size_t lds = (size_t)((Kp + 3) & ~3) * sizeof(uint16_t) +
+                     (use_prefix ? (size_t)(K + 1) * sizeof(double) : 0);
+  const dim3 grid((unsigned)R);
+  const int kpl = (Kp >= 64 && Kp <= 2048) ? Kp / 64 : 0;   // keys per lane; 0: sort in LDS
   switch (bits) {
-    case 2: hipLaunchKernelGGL(kmeans_rows_kernel<2>, grid, block, lds, stream, w, ldw, K, Kp,
-                               max_iters, idx, codebook, iters_done); break;
-    case 3: hipLaunchKernelGGL(kmeans_rows_kernel<3>, grid, block, lds, stream, w, ldw, K, Kp,
-                               max_iters, idx, codebook, iters_done); break;
-    case 4: hipLaunchKernelGGL(kmeans_rows_kernel<4>, grid, block, lds, stream, w, ldw, K, Kp,
-                               max_iters, idx, codebook, iters_done); break;
+    case 2: launch_bits<2>(kpl, grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 3: launch_bits<3>(kpl, grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
+    case 4: launch_bits<4>(kpl, grid, lds, stream, w, ldw, K, Kp, use_prefix, max_iters, idx, codebook, iters_done); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
