@@ -47,7 +47,8 @@ import numpy as np
 
 __all__ = [
     "sylvester_hadamard", "block_size", "bf16_bits_to_f64", "f16_bits_to_f64",
-    "rotation_precondition", "rotate", "rotate_fp64", "round_int_pow2_to_f32",
+    "rotation_precondition", "rotate", "rotate_values", "smooth_and_sign", "rotate_fp64",
+    "round_int_pow2_to_f32",
     "quantize", "rotate_quantize", "pack_codes", "unpack_codes", "unpack_indices",
     "dequantize", "expert_gemm", "dense_gemm", "gemm_entry", "lut_gemm_table",
     "lut_gemm_buckets", "route", "silu_mul_bf16", "round_f64_to_bf16_bits", "combine",
@@ -89,13 +90,14 @@ def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
-def rotation_precondition(xb: np.ndarray, b: int) -> np.ndarray:
-    """True where fp64 summation of a block of bf16 values is exact in any order.
+def rotation_precondition(xb: np.ndarray, b: int, sig_bits: int = 8) -> np.ndarray:
+    """True where fp64 summation of a block of values is exact in any order.
 
-    Every bf16 value with exponent e (|x| in [2^e, 2^(e+1))) is a multiple of
-    2^(e-7); the block's partial sums are then integers in units of 2^(e_min-7) whose
-    size is below 2^(log2 b + e_max - e_min + 8).  They stay below 2^53 when
-    e_max - e_min <= 45 - log2 b.  xb: [..., b] fp64."""
+    Every value with exponent e (|x| in [2^e, 2^(e+1))) and sig_bits significant bits
+    (8 for bf16, 24 for fp32) is a multiple of 2^(e-sig_bits+1); the block's partial
+    sums are then integers in units of 2^(e_min-sig_bits+1) whose size is below
+    2^(log2 b + e_max - e_min + sig_bits).  They stay below 2^53 when
+    e_max - e_min <= 53 - sig_bits - log2 b (45 - log2 b for bf16).  xb: [..., b] fp64."""
     a = np.abs(xb)
     nz = a > 0
     _, ex = np.frexp(a)
@@ -103,7 +105,7 @@ def rotation_precondition(xb: np.ndarray, b: int) -> np.ndarray:
     big = np.int64(1 << 40)
     emax = np.where(nz, e, -big).max(axis=-1)
     emin = np.where(nz, e, big).min(axis=-1)
-    spread_ok = (emax - emin) <= (45 - int(round(math.log2(b))))
+    spread_ok = (emax - emin) <= (53 - sig_bits - int(round(math.log2(b))))
     return spread_ok | ~nz.any(axis=-1)
 
 
@@ -127,14 +129,15 @@ def round_int_pow2_to_f32(n: int, s: int) -> np.float32:
         return np.float32(sign * math.ldexp(m, q)) if q < 200 else np.float32(sign * np.inf)
 
 
-def _exact_block_f32(xblock: np.ndarray, H: np.ndarray) -> np.ndarray:
-    """Exact H @ x for one block of bf16-valued fp64 inputs, rounded once to fp32."""
+def _exact_block_f32(xblock: np.ndarray, H: np.ndarray, sig_bits: int = 8) -> np.ndarray:
+    """Exact H @ x for one block of fp64 inputs with sig_bits significant bits (bf16: 8,
+    fp32: 24), rounded once to fp32."""
     vals = [float(v) for v in xblock]
     nz = [v for v in vals if v != 0.0]
     out = np.zeros(len(vals), dtype=np.float32)
     if not nz:
         return out
-    s = min(math.frexp(abs(v))[1] - 1 for v in nz) - 7
+    s = min(math.frexp(abs(v))[1] - 1 for v in nz) - (sig_bits - 1)
     ints = [int(math.ldexp(v, -s)) for v in vals]   # exact: each v is a multiple of 2^s
     for j in range(len(vals)):
         acc = 0
@@ -153,24 +156,49 @@ def rotate_fp64(x: np.ndarray, b: int) -> np.ndarray:
     return (x.reshape(T, K // b, b) @ H).reshape(T, K)   # H is symmetric
 
 
-def rotate(x_bits: np.ndarray, b: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Exact block rotation of bf16 tokens, rounded once to fp32.
+def rotate_values(x: np.ndarray, b: int, sig_bits: int = 8) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact block rotation of tokens whose values (fp64 [T][K]) have sig_bits
+    significant bits, rounded once to fp32.
 
     Returns (u32 [T][K] float32, precondition_ok [T][K/b] bool).  Blocks whose exponent
     spread breaks the fp64 exactness bound are recomputed in exact integer arithmetic,
     so u32 is always the correctly rounded exact rotation."""
-    x = bf16_bits_to_f64(x_bits)
     T, K = x.shape
     if K % b:
         raise ValueError("block must divide K")
     xb = x.reshape(T, K // b, b)
-    ok = rotation_precondition(xb, b)
+    ok = rotation_precondition(xb, b, sig_bits)
     u32 = rotate_fp64(x, b).astype(np.float32).reshape(T, K // b, b)
     if not ok.all():
         H = sylvester_hadamard(b)
         for t, j in zip(*np.nonzero(~ok)):
-            u32[t, j] = _exact_block_f32(xb[t, j], H)
+            u32[t, j] = _exact_block_f32(xb[t, j], H, sig_bits)
     return u32.reshape(T, K), ok
+
+
+def rotate(x_bits: np.ndarray, b: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact block rotation of bf16 tokens, rounded once to fp32 (see rotate_values)."""
+    return rotate_values(bf16_bits_to_f64(x_bits), b, 8)
+
+
+def smooth_and_sign(x_bits: np.ndarray, smooth: Optional[np.ndarray] = None,
+                    signs: Optional[np.ndarray] = None) -> Tuple[np.ndarray, int]:
+    """The per-channel transforms applied before the Hadamard blocks (CodeQuant2,
+    Figure 1: rotation and scaling fused for outlier smoothing; Table 5 caption: a fixed
+    random rotation with SmoothQuant scaling).
+
+    v_c = fp32(x_c * m_c) with fp32 multipliers m (one rounding; skipped when smooth is
+    None), negated where bit c of the LSB-first bitmask signs is set.  Returns (v as
+    fp64 [T][K], significant bits of v: 24 after smoothing, else 8)."""
+    x32 = bf16_bits_to_f64(x_bits).astype(np.float32)
+    K = x32.shape[1]
+    if smooth is not None:
+        x32 = (x32 * np.asarray(smooth, dtype=np.float32)[None, :K]).astype(np.float32)
+    v = x32.astype(np.float64)
+    if signs is not None:
+        bits = np.unpackbits(np.asarray(signs, dtype=np.uint8), bitorder="little")[:K].astype(bool)
+        v = np.where(bits[None, :], -v, v)
+    return v, (24 if smooth is not None else 8)
 
 
 # ---------------------------------------------------------------------------
@@ -216,13 +244,18 @@ def unpack_codes(packed: np.ndarray, K: int, act_bits: int) -> np.ndarray:
     return out[:, :K]
 
 
-def rotate_quantize(x_bits: np.ndarray, had_block: int, act_bits: int):
-    """Rotation followed by quantisation and packing.
+def rotate_quantize(x_bits: np.ndarray, had_block: int, act_bits: int,
+                    smooth: Optional[np.ndarray] = None, signs: Optional[np.ndarray] = None):
+    """(Optional smoothing and random signs,) rotation, quantisation and packing.
 
     Returns dict(codes=packed uint8, q=int8 [T][K], scale=float32 [T], u32, b, ok)."""
     T, K = x_bits.shape
     b = block_size(K, had_block)
-    u32, ok = rotate(x_bits, b)
+    if smooth is None and signs is None:
+        u32, ok = rotate(x_bits, b)
+    else:
+        v, sig = smooth_and_sign(x_bits, smooth, signs)
+        u32, ok = rotate_values(v, b, sig)
     q, scale = quantize(u32, b, act_bits)
     return dict(codes=pack_codes(q, act_bits), q=q, scale=scale, u32=u32, b=b, ok=ok)
 
