@@ -23,7 +23,7 @@ PATH_AUTO, PATH_LUT, PATH_MFMA = 0, 1, 2
 AUTO_MAX_LUT_ROWS = 32
 
 # every symbol include/cbq.h declares
-EXPORTED = ("cbq_rotate_quantize", "cbq_route_workspace", "cbq_moe_route_gather",
+EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_route_workspace", "cbq_moe_route_gather",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
             "cbq_kmeans_codebooks", "cbq_status_string", "cbq_last_error", "cbq_version")
 
@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     W = ctypes.POINTER(cbq_weights)
     sig = {
         "cbq_rotate_quantize": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
+        "cbq_rotate_quantize_ex": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp, vp,
+                                                  vp]),
         "cbq_route_workspace": (sz, [i64, i32, i32, i32]),
         "cbq_moe_route_gather": (ctypes.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                 vp, sz, vp]),
@@ -122,10 +124,13 @@ class CodebookWeights:
 # ---------------------------------------------------------------------------
 def rotate_quantize(x: torch.Tensor, act_bits: int = 4, had_block: int = 0,
                     codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
-                    precond: Optional[torch.Tensor] = None, stream=None):
-    """x: bf16 (or int16 bit patterns) [T][K] on the GPU -> (codes uint8, scales fp32)."""
+                    precond: Optional[torch.Tensor] = None, smooth: Optional[torch.Tensor] = None,
+                    signs: Optional[torch.Tensor] = None, stream=None):
+    """x: bf16 (or int16 bit patterns) [T][K] on the GPU -> (codes uint8, scales fp32).
+
+    smooth (fp32 [K]) and signs (uint8 [K/8] bitmask) select cbq_rotate_quantize_ex."""
     lib = load_library()
-    _require_gpu(x)
+    _require_gpu(x, smooth, signs)
     T, K = x.shape
     ldx = x.stride(0)
     if x.stride(1) != 1:
@@ -134,8 +139,13 @@ def rotate_quantize(x: torch.Tensor, act_bits: int = 4, had_block: int = 0,
         codes = torch.empty((T, K * act_bits // 8), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((T,), dtype=torch.float32, device=x.device)
-    _check(lib.cbq_rotate_quantize(_ptr(x), T, K, ldx, had_block, act_bits, _ptr(codes),
-                                   _ptr(scales), _ptr(precond), _stream(stream)))
+    if smooth is None and signs is None:
+        _check(lib.cbq_rotate_quantize(_ptr(x), T, K, ldx, had_block, act_bits, _ptr(codes),
+                                       _ptr(scales), _ptr(precond), _stream(stream)))
+    else:
+        _check(lib.cbq_rotate_quantize_ex(_ptr(x), T, K, ldx, had_block, act_bits, _ptr(smooth),
+                                          _ptr(signs), _ptr(codes), _ptr(scales), _ptr(precond),
+                                          _stream(stream)))
     return codes, scales
 
 

@@ -55,9 +55,10 @@ CBQ_EXPORT const char* cbq_last_error(void) { return g_err; }
 
 CBQ_EXPORT int cbq_version(void) { return 100; }
 
-CBQ_EXPORT int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
-                                   int32_t had_block, int32_t act_bits, uint8_t* codes,
-                                   float* scales, uint32_t* precond_violations, void* stream) {
+CBQ_EXPORT int cbq_rotate_quantize_ex(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
+                                      int32_t had_block, int32_t act_bits, const float* smooth,
+                                      const uint8_t* signs, uint8_t* codes, float* scales,
+                                      uint32_t* precond_violations, void* stream) {
   g_err[0] = 0;
   if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
   if (T > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "T must be < 2^31");
@@ -68,13 +69,22 @@ CBQ_EXPORT int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int6
   int b = had_block;
   if (b == 0) b = K & -K;
   if (!pow2(b) || K % b) return fail(CBQ_EINVAL, "had_block must be 0 or a power of two dividing K (got %d)", had_block);
+  if ((smooth && !aligned16(smooth)) || (signs && (reinterpret_cast<uintptr_t>(signs) & 3u)))
+    return fail(CBQ_EINVAL, "smooth must be 16-byte and signs 4-byte aligned");
   if (T == 0) return CBQ_OK;
   if (!x || !codes || !scales) return fail(CBQ_EINVAL, "x, codes and scales must be non-null");
   if (!aligned16(x) || !aligned16(codes)) return fail(CBQ_EINVAL, "x and codes must be 16-byte aligned");
-  hipError_t e = cbq::launch_rotate_quantize(x, T, K, ldx, b, act_bits, codes, scales,
-                                             precond_violations, (hipStream_t)stream);
+  hipError_t e = cbq::launch_rotate_quantize(x, T, K, ldx, b, act_bits, smooth, signs, codes,
+                                             scales, precond_violations, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "rotate_quantize launch");
   return CBQ_OK;
+}
+
+CBQ_EXPORT int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
+                                   int32_t had_block, int32_t act_bits, uint8_t* codes,
+                                   float* scales, uint32_t* precond_violations, void* stream) {
+  return cbq_rotate_quantize_ex(x, T, K, ldx, had_block, act_bits, nullptr, nullptr, codes,
+                                scales, precond_violations, stream);
 }
 
 CBQ_EXPORT size_t cbq_route_workspace(int64_t T, int32_t E, int32_t topk, int32_t n_shared) {

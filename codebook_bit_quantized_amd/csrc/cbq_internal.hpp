@@ -31,7 +31,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t ldx, int b,
-                                  int act_bits, uint8_t* codes, float* scales, uint32_t* precond,
+                                  int act_bits, const float* smooth, const uint8_t* signs,
+                                  uint8_t* codes, float* scales, uint32_t* precond,
                                   hipStream_t stream);
 
 size_t route_workspace_bytes(int64_t T, int E);

@@ -11,6 +11,12 @@
 // lane exchange per further stage (DPP for lane distances 1, 2 and 8, ds_swizzle for
 // 4 and 16, a permute for 32) and LDS exchanges across waves beyond 64 lanes.
 //
+// Optionally, before the rotation, each channel is multiplied by an fp32 smoothing
+// factor (one fp32 rounding; the exactness bound then becomes 29 - log2(b) binades)
+// and/or negated by a random sign bit (CodeQuant2, Figure 1: rotation and scaling
+// fused for outlier smoothing; Table 5 caption: a fixed random rotation with
+// SmoothQuant scaling).
+//
 // The quantiser follows one fixed IEEE fp32 sequence: v = fp32(u), M = max|v|,
 // s = M / Q, r = fp32(v / s), q = clamp(rint_even(r)).  The quotient is formed as
 // fp64(v) * fp64(1 / s) and then rounded to fp32: for fp32 v and s the exact quotient
@@ -78,7 +84,8 @@ __device__ __forceinline__ void exp_range(double x, int& emin, int& emax) {
 // G: lanes per token (a power of two <= 64, or a multiple of 64 = the workgroup).
 __global__ void __launch_bounds__(512)
 rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, int K, int logb,
-                       int G, int act_bits, float c_b, uint8_t* __restrict__ codes,
+                       int G, int act_bits, float c_b, const float* __restrict__ smooth,
+                       const uint8_t* __restrict__ signs, uint8_t* __restrict__ codes,
                        float* __restrict__ scales, uint32_t* __restrict__ precond) {
   extern __shared__ double xchg[];          // cross-wave butterflies: [8][blockDim]
   __shared__ float red_max[8];
@@ -103,20 +110,36 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
   double v[32];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (active ? t * ldx + (int64_t)j * 32 : 0));
+    float f[32];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const u32x4 p = active ? src[h] : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[8 * h + 2 * i] = (double)__builtin_bit_cast(float, p[i] << 16);
-        v[8 * h + 2 * i + 1] = (double)__builtin_bit_cast(float, p[i] & 0xFFFF0000u);
+        f[8 * h + 2 * i] = __builtin_bit_cast(float, p[i] << 16);
+        f[8 * h + 2 * i + 1] = __builtin_bit_cast(float, p[i] & 0xFFFF0000u);
       }
     }
+    // optional per-channel transforms before the rotation: v = fp32(x * m), negated
+    // where the channel's sign bit is set
+    if (smooth != nullptr && active) {
+      const f32x4* ms = reinterpret_cast<const f32x4*>(smooth + j * 32);
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const f32x4 m = ms[h];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[4 * h + i] = __fmul_rn(f[4 * h + i], m[i]);
+      }
+    }
+    uint32_t sg = 0;
+    if (signs != nullptr && active) sg = reinterpret_cast<const uint32_t*>(signs)[j];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = (double)((sg >> i) & 1u ? -f[i] : f[i]);
   }
 
   // ---- optional exactness check: exponent spread inside each block ----
   if (precond != nullptr) {
-    const int limit = 45 - logb;
+    const int limit = (smooth != nullptr ? 29 : 45) - logb;   // 53 - significant bits - log2 b
     if (b <= 32) {                           // whole blocks inside this thread
       int emin = 1 << 20, emax = -(1 << 20);
 #pragma unroll
@@ -253,7 +276,8 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
 }
 
 hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t ldx, int b,
-                                  int act_bits, uint8_t* codes, float* scales, uint32_t* precond,
+                                  int act_bits, const float* smooth, const uint8_t* signs,
+                                  uint8_t* codes, float* scales, uint32_t* precond,
                                   hipStream_t stream) {
   const int nthr = K / 32;
   int logb = 0;
@@ -275,7 +299,7 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
     if (b > 2048) lds = (size_t)threads * 8 * sizeof(double);
   }
   hipLaunchKernelGGL(rotate_quantize_kernel, dim3((unsigned)blocks), dim3(threads), lds, stream, x,
-                     ldx, T, K, logb, G, act_bits, c_b, codes, scales, precond);
+                     ldx, T, K, logb, G, act_bits, c_b, smooth, signs, codes, scales, precond);
   return hipGetLastError();
 }
 

@@ -85,8 +85,7 @@ typedef struct {
  *  x          : bf16 [T][ldx] (ldx >= K, ldx % 8 == 0, 16-byte aligned); row t holds
  *               one token's K channels.
  *  had_block  : 0 -> rotation block b = K & -K (largest power of two dividing K);
- *               otherwise b itself (a power of two dividing K; 1 = no rotation);
- *               b <= 4096.
+ *               otherwise b itself (a power of two dividing K; 1 = no rotation).
  *  act_bits   : 4 (codes in [-8, 7], Q = 7) or 8 (codes in [-127, 127], Q = 127).
  *  codes      : [T][K*act_bits/8] bytes, 16-byte aligned.  A4: two's-complement
  *               nibbles, channel 2j in the low nibble of byte j; A8: int8.
@@ -105,6 +104,26 @@ typedef struct {
 int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
                         int32_t had_block, int32_t act_bits, uint8_t* codes, float* scales,
                         uint32_t* precond_violations, void* stream);
+
+/*
+ * cbq_rotate_quantize_ex - cbq_rotate_quantize with per-channel transforms before the
+ * rotation.  Passage: CodeQuant2, Figure 1 (rotation and scaling fused into the model
+ * for outlier smoothing) and Table 5 caption (the base configuration: a fixed random
+ * rotation with SmoothQuant scaling).
+ *
+ *  smooth : optional fp32 [K] multipliers m (16-byte aligned): channel c becomes
+ *           fp32(x_c * m_c), one fp32 rounding (a SmoothQuant factor 1/s_c).
+ *  signs  : optional [K/8] bytes (4-byte aligned), LSB-first bit c set -> channel c is
+ *           negated (a random-sign Hadamard, H D).
+ *  Then u = (I (x) H_b) v exactly and the quantiser of cbq_rotate_quantize.  With smooth,
+ *  the values have 24 significant bits and the fp64 transform is exact when a block's
+ *  nonzero exponents spread at most 29 - log2(b) binades (the precondition counter
+ *  tests that bound).  NULL, NULL gives cbq_rotate_quantize exactly.
+ */
+int cbq_rotate_quantize_ex(const uint16_t* x, int64_t T, int32_t K, int64_t ldx, int32_t had_block,
+                           int32_t act_bits, const float* smooth, const uint8_t* signs,
+                           uint8_t* codes, float* scales, uint32_t* precond_violations,
+                           void* stream);
 
 /*
  * cbq_moe_route_gather - top-k routing and per-expert row lists.

@@ -64,6 +64,16 @@ def test_rotate_quantize_validation():
     assert rq(None, 0, 256, 256, 0, 4, None, None, None, None) == cbq.CBQ_OK  # T = 0 no-op
 
 
+def test_rotate_quantize_ex_validation():
+    lib = _lib()
+    P, U = _Fake.P, _Fake.UNALIGNED
+    ex = lib.cbq_rotate_quantize_ex
+    assert ex(P, 4, 256, 256, 0, 4, U, None, P, P, None, None) == cbq.CBQ_EINVAL    # smooth alignment
+    assert ex(P, 4, 256, 256, 0, 4, None, ctypes.c_void_p(0x1002), P, P, None, None) == cbq.CBQ_EINVAL
+    assert ex(P, 4, 250, 256, 0, 4, P, P, P, P, None, None) == cbq.CBQ_EINVAL      # K % 32
+    assert ex(P, 0, 256, 256, 0, 4, P, P, P, P, None, None) == cbq.CBQ_OK          # empty
+
+
 def test_route_validation():
     lib = _lib()
     P = _Fake.P
