@@ -256,6 +256,71 @@ def cpu_baseline_dense(wl, weights_np):
                        f"({ntok} tokens, {dt:.1f} s, numpy fp64, BLAS threads {threads})")
 
 
+def bench_cpu_lut(args, cbq, torch):
+    """The host LUT GEMM on the 2560 -> 9728 decode linear (4-bit, A4), T = 1/4/16, all
+    host threads: tokens/s and weight GB/s against this host's measured streaming read
+    rate; beside it a bf16 GEMM of the dequantised weights (torch on the CPU: the dense
+    model the method replaces) and the oracle."""
+    import oracle
+    wl = datagen.WORKLOADS["dense2560x9728"]
+    ws = datagen.dense_weights(wl, "gate_up")
+    nbytes_w = ws.idx.nbytes + ws.codebook.nbytes
+    big = np.ones(1 << 28, dtype=np.float32)                  # 1 GiB
+    big.sum()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        big.sum()
+    stream_gbs = 3 * big.nbytes / (time.perf_counter() - t0) / 1e9
+    del big
+    W = torch.from_numpy(oracle.dequantize(oracle.unpack_indices(ws.idx[0], ws.K, ws.bits),
+                                           ws.codebook[0]).astype(np.float32)).to(torch.bfloat16)
+    rows = {}
+    for T in wl.T_list:
+        x = datagen.dense_tokens(wl, T)
+        rq = oracle.rotate_quantize(x, 0, wl.act_bits)
+        out = np.empty((T, wl.N), dtype=np.float32)
+        cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, ws.idx, ws.codebook, ws.K, ws.bits, out=out)
+        reps = max(5, args.steps)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, ws.idx, ws.codebook, ws.K, ws.bits, out=out)
+        t_lut = (time.perf_counter() - t0) / reps
+        xb = torch.from_numpy(oracle.bf16_bits_to_f64(x).astype(np.float32)).to(torch.bfloat16)
+        torch.matmul(xb, W.t())
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            torch.matmul(xb, W.t())
+        t_bf16 = (time.perf_counter() - t0) / reps
+        rows[T] = dict(lut_us=round(t_lut * 1e6, 1), bf16_us=round(t_bf16 * 1e6, 1),
+                       speedup_vs_bf16=round(t_bf16 / t_lut, 2),
+                       weight_gbs=round(nbytes_w / t_lut / 1e9, 1))
+    T = max(wl.T_list)
+    t_lut = rows[T]["lut_us"] / 1e6
+    cpu = None
+    if not args.no_cpu_baseline:
+        x = datagen.dense_tokens(wl, T)
+        t0 = time.perf_counter()
+        rq = oracle.rotate_quantize(x, 0, wl.act_bits)
+        oracle.expert_gemm(rq["q"].astype(np.int64), rq["scale"], None, None, ws.idx, ws.codebook,
+                           ws.K, ws.bits)
+        dt = time.perf_counter() - t0
+        cpu = dict(value=round(T / dt, 2), unit="tokens/s", cores=1, kind="oracle",
+                   sample=f"oracle rotate+quantise and dequantise-then-matmul of the 2560->9728 "
+                          f"linear for {T} tokens ({dt:.2f} s, numpy fp64)")
+    gbs = nbytes_w / t_lut / 1e9
+    line = dict(metric="CPU LUT GEMM tokens/s", value=round(T / t_lut, 1), unit="tokens/s",
+                n_gpus=0, steps=max(5, args.steps), warmup=1, ms_per_step=round(t_lut * 1e3, 4),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+                config=dict(workload="cpu_lut_dense2560x9728", K=wl.K, N=wl.N, bits=wl.bits,
+                            act_bits=wl.act_bits, host_threads=os.cpu_count(), per_batch=rows),
+                roofline=dict(bound="dram", achieved=round(gbs, 1), peak=round(stream_gbs, 1),
+                              unit="GB/s", frac=round(gbs / stream_gbs, 4), traffic=None,
+                              kernel="cpu_lut_gemm (weights once per call)",
+                              peak_note="host streaming read rate measured in this run"),
+                cpu_baseline=cpu, host=platform.node())
+    print(json.dumps(line))
+
+
 def bench_kmeans(args, cbq, torch):
     """Codebook construction for every gate matrix of the workload (E + S experts x F rows
     of H bf16 weights, 2^bits_gate_up clusters): rows/s, against the time to stream the
@@ -315,6 +380,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefill-sample", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--cpu-lut", action="store_true",
+                    help="measure the host (CPU) LUT GEMM on the dense decode linear instead")
     ap.add_argument("--kmeans", action="store_true",
                     help="measure offline codebook construction (per-row K-means) instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -329,6 +396,9 @@ def main():
     import torch
     import codebook_bit_quantized_amd as cbq
 
+    if args.cpu_lut:
+        bench_cpu_lut(args, cbq, torch)
+        return
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)

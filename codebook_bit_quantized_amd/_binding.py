@@ -25,7 +25,8 @@ AUTO_MAX_LUT_ROWS = 32
 # every symbol include/cbq.h declares
 EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_route_workspace", "cbq_moe_route_gather",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
-            "cbq_kmeans_codebooks", "cbq_status_string", "cbq_last_error", "cbq_version")
+            "cbq_kmeans_codebooks", "cbq_cpu_lut_gemm", "cbq_status_string", "cbq_last_error",
+            "cbq_version")
 
 
 class CbqError(RuntimeError):
@@ -65,6 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                  i64, vp, sz, vp]),
         "cbq_moe_combine": (ctypes.c_int, [vp, vp, vp, i64, i32, i32, i32, vp, vp]),
         "cbq_kmeans_codebooks": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
+        "cbq_cpu_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, W, vp, i64, i32]),
         "cbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "cbq_last_error": (ctypes.c_char_p, []),
         "cbq_version": (ctypes.c_int, []),
@@ -235,6 +237,27 @@ def kmeans_codebooks(w: torch.Tensor, bits: int, max_iters: int = 50, idx: Optio
     _check(lib.cbq_kmeans_codebooks(_ptr(w), R, K, w.stride(0), bits, max_iters, _ptr(idx),
                                     _ptr(codebook), _ptr(iters_done), _stream(stream)))
     return CodebookWeights(idx=idx, codebook=codebook, K=K, bits=bits)
+
+
+def cpu_lut_gemm(codes, scales, act_bits: int, idx, codebook, K: int, bits: int,
+                 n_threads: int = 0, out=None):
+    """The LUT GEMM on host cores (cbq_cpu_lut_gemm).  numpy arrays: codes uint8
+    [T][K*act_bits/8], scales float32 [T], idx uint8 [N][K*bits/8] (or [1][N][...]),
+    codebook uint16 [N][2^bits]; returns float32 [T][N]."""
+    import numpy as np
+    lib = load_library()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.uint8).reshape(-1, K * bits // 8)
+    codebook = np.ascontiguousarray(codebook).view(np.uint16).reshape(-1, 1 << bits)
+    T, N = codes.shape[0], idx.shape[0]
+    if out is None:
+        out = np.empty((T, N), dtype=np.float32)
+    w = cbq_weights(idx.ctypes.data, codebook.ctypes.data, 1, N, K, bits)
+    _check(lib.cbq_cpu_lut_gemm(ctypes.c_void_p(codes.ctypes.data), ctypes.c_void_p(scales.ctypes.data),
+                                act_bits, T, ctypes.byref(w), ctypes.c_void_p(out.ctypes.data),
+                                out.strides[0] // 4, n_threads))
+    return out
 
 
 def moe_ffn(x: torch.Tensor, logits: torch.Tensor, gate: CodebookWeights, up: CodebookWeights,

@@ -2,9 +2,9 @@
 
     python -m codebook_bit_quantized_amd.build [--jobs N]
 
-Every translation unit under csrc/ is compiled by hipcc for gfx950 only and linked
-into codebook_bit_quantized_amd/_lib/libcbq.so.  Packed-fp32 instructions are
-disabled for the device code.
+Every HIP translation unit under csrc/ is compiled by hipcc for gfx950 only (packed-fp32
+instructions disabled for the device code), the host-only C++ files by g++, and all are
+linked into codebook_bit_quantized_amd/_lib/libcbq.so.
 """
 from __future__ import annotations
 
@@ -31,13 +31,22 @@ CFLAGS = [
 ]
 
 
+CXX = shutil.which("g++") or "g++"
+CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread",
+            "-I", os.path.join(ROOT, "include")]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):       # host-only code (the CPU LUT kernel)
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -52,7 +61,7 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [HIPCC, "-shared", "-fPIC", "-pthread", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include "../../include/cbq.h"
+#include "cpu_lut.hpp"
 #include "cbq_internal.hpp"
 
 #define CBQ_EXPORT extern "C" __attribute__((visibility("default")))
@@ -207,6 +208,25 @@ CBQ_EXPORT int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int
   hipError_t e = cbq::launch_kmeans(w, R, K, ldw, bits, max_iters, idx, codebook, iters_done,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kmeans_codebooks launch");
+  return CBQ_OK;
+}
+
+CBQ_EXPORT int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits,
+                                int64_t T, const cbq_weights* W, float* out, int64_t ldo,
+                                int32_t n_threads) {
+  g_err[0] = 0;
+  if (!W) return fail(CBQ_EINVAL, "W must be non-null");
+  if (int rc = check_weights(W, 0)) return rc;
+  if (W->E != 1) return fail(CBQ_EUNSUPPORTED, "the CPU kernel takes one weight set (E = 1, got %d)", W->E);
+  if (act_bits != 4 && act_bits != 8) return fail(CBQ_EINVAL, "act_bits must be 4 or 8 (got %d)", act_bits);
+  if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0");
+  if (ldo < W->N) return fail(CBQ_EINVAL, "ldo must be >= N");
+  if (n_threads < 0) return fail(CBQ_EINVAL, "n_threads must be >= 0");
+  if (T == 0) return CBQ_OK;
+  if (!codes || !scales || !out) return fail(CBQ_EINVAL, "codes, scales and out must be non-null");
+  if (!cbq::cpu_lut_supported()) return fail(CBQ_EUNSUPPORTED, "the CPU kernel needs AVX2, FMA, F16C and BMI2");
+  cbq::cpu_lut_gemm_impl(codes, scales, act_bits, T, W->N, W->K, W->bits, W->idx, W->codebook, out,
+                         ldo, n_threads);
   return CBQ_OK;
 }
 

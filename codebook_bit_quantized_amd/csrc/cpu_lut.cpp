@@ -1,0 +1,170 @@
+// Codebook-LUT GEMM on host cores (x86-64, AVX2).
+//
+// CodeQuant abstract and the AI Radio episode ("Improvements"): the method comes with
+// dedicated LUT kernels for GPU and CPU, which look products up instead of computing
+// them.  As on the GPU, the table held in registers is each weight row's codebook,
+// split into its low and high bytes: vpshufb looks up 32 indices per instruction in
+// each 16-entry byte table, two unpacks rebuild the fp16 centroids, F16C widens them
+// and FMAs multiply them by the activation codes (exact integers; each product is exact
+// in fp32, only the fp32 summation order differs from the definition).  The weights are
+// dequantised once per row and reused by up to 8 tokens held in registers.
+//
+// Index unpacking: 4-bit nibbles with byte shuffles; 3- and 2-bit fields with BMI2
+// pdep (eight indices per 24 or 16 bits).
+#include "cpu_lut.hpp"
+
+#include <immintrin.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+namespace cbq {
+
+bool cpu_lut_supported() {
+  __builtin_cpu_init();
+  return __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+         __builtin_cpu_supports("f16c") && __builtin_cpu_supports("bmi2");
+}
+
+namespace {
+
+// 32 consecutive indices of a row (starting at index k, k % 32 == 0) as bytes 0..31.
+template <int BITS>
+__attribute__((target("avx2,bmi2"))) inline __m256i load_indices(const uint8_t* row, int k) {
+  if constexpr (BITS == 4) {
+    const __m128i p = _mm_loadu_si128(reinterpret_cast<const __m128i*>(row + k / 2));
+    const __m128i m = _mm_set1_epi8(0x0F);
+    const __m128i lo = _mm_and_si128(p, m);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(p, 4), m);
+    return _mm256_set_m128i(_mm_unpackhi_epi8(lo, hi), _mm_unpacklo_epi8(lo, hi));
+  } else {
+    constexpr int GB = BITS == 3 ? 3 : 2;                 // bytes per 8 indices
+    constexpr uint64_t MASK = BITS == 3 ? 0x0707070707070707ull : 0x0303030303030303ull;
+    const uint8_t* p = row + (int64_t)k * BITS / 8;
+    uint64_t q[4];
+    for (int g = 0; g < 4; ++g) {
+      uint64_t f = 0;
+      for (int b = 0; b < GB; ++b) f |= (uint64_t)p[g * GB + b] << (8 * b);
+      q[g] = _pdep_u64(f, MASK);
+    }
+    return _mm256_set_epi64x((long long)q[3], (long long)q[2], (long long)q[1], (long long)q[0]);
+  }
+}
+
+// One row against TB tokens.  Each token keeps NA independent partial sums (more for
+// fewer tokens) so the FMA latency chain never limits the loop; at most 8 accumulators.
+template <int BITS, int TB>
+__attribute__((target("avx2,fma,f16c,bmi2")))
+inline void row_tokens(const float* a, const float* scales, int64_t t0, int K, const uint8_t* row,
+                       __m256i tlo, __m256i thi, float* out, int64_t ldo, int64_t n) {
+  constexpr int NA = TB <= 2 ? 4 : (TB <= 4 ? 2 : 1);
+  __m256 acc[TB][NA];
+#pragma GCC unroll 8
+  for (int t = 0; t < TB; ++t)
+#pragma GCC unroll 4
+    for (int p = 0; p < NA; ++p) acc[t][p] = _mm256_setzero_ps();
+  for (int k = 0; k < K; k += 32) {
+    const __m256i ix = load_indices<BITS>(row, k);
+    const __m256i vlo = _mm256_shuffle_epi8(tlo, ix);
+    const __m256i vhi = _mm256_shuffle_epi8(thi, ix);
+    const __m256i h0 = _mm256_unpacklo_epi8(vlo, vhi);     // k 0..7  | k 16..23
+    const __m256i h1 = _mm256_unpackhi_epi8(vlo, vhi);     // k 8..15 | k 24..31
+    const __m256 w[4] = {_mm256_cvtph_ps(_mm256_castsi256_si128(h0)),
+                         _mm256_cvtph_ps(_mm256_castsi256_si128(h1)),
+                         _mm256_cvtph_ps(_mm256_extracti128_si256(h0, 1)),
+                         _mm256_cvtph_ps(_mm256_extracti128_si256(h1, 1))};
+#pragma GCC unroll 8
+    for (int t = 0; t < TB; ++t) {
+      const float* at = a + (t0 + t) * (int64_t)K + k;
+#pragma GCC unroll 4
+      for (int i = 0; i < 4; ++i)
+        acc[t][i % NA] = _mm256_fmadd_ps(w[i], _mm256_loadu_ps(at + 8 * i), acc[t][i % NA]);
+    }
+  }
+#pragma GCC unroll 8
+  for (int t = 0; t < TB; ++t) {
+    __m256 v = acc[t][0];
+#pragma GCC unroll 4
+    for (int p = 1; p < NA; ++p) v = _mm256_add_ps(v, acc[t][p]);
+    const __m128 s4 = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+    const __m128 s2 = _mm_add_ps(s4, _mm_movehl_ps(s4, s4));
+    const __m128 s1 = _mm_add_ss(s2, _mm_shuffle_ps(s2, s2, 1));
+    out[(t0 + t) * ldo + n] = scales[t0 + t] * _mm_cvtss_f32(s1);
+  }
+}
+
+template <int BITS>
+__attribute__((target("avx2,fma,f16c,bmi2")))
+void rows_kernel(const float* a, const float* scales, int64_t T, int64_t n0, int64_t n1, int K,
+                 const uint8_t* idx, const uint16_t* codebook, float* out, int64_t ldo) {
+  constexpr int L = 1 << BITS;
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  for (int64_t n = n0; n < n1; ++n) {
+    alignas(16) uint8_t lo[16] = {0}, hi[16] = {0};
+    for (int c = 0; c < L; ++c) {
+      lo[c] = (uint8_t)(codebook[n * L + c] & 0xFF);
+      hi[c] = (uint8_t)(codebook[n * L + c] >> 8);
+    }
+    const __m256i tlo = _mm256_broadcastsi128_si256(_mm_load_si128(reinterpret_cast<const __m128i*>(lo)));
+    const __m256i thi = _mm256_broadcastsi128_si256(_mm_load_si128(reinterpret_cast<const __m128i*>(hi)));
+    const uint8_t* row = idx + n * row_bytes;
+    int64_t t0 = 0;
+    for (; t0 + 8 <= T; t0 += 8) row_tokens<BITS, 8>(a, scales, t0, K, row, tlo, thi, out, ldo, n);
+    switch (T - t0) {
+      case 1: row_tokens<BITS, 1>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      case 2: row_tokens<BITS, 2>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      case 3: row_tokens<BITS, 3>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      case 4: row_tokens<BITS, 4>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      case 5: row_tokens<BITS, 5>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      case 6: row_tokens<BITS, 6>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      case 7: row_tokens<BITS, 7>(a, scales, t0, K, row, tlo, thi, out, ldo, n); break;
+      default: break;
+    }
+  }
+}
+
+}  // namespace
+
+void cpu_lut_gemm_impl(const uint8_t* codes, const float* scales, int act_bits, int64_t T,
+                       int64_t N, int K, int bits, const uint8_t* idx, const uint16_t* codebook,
+                       float* out, int64_t ldo, int n_threads) {
+  // activation codes -> fp32 (exact small integers), natural channel order
+  std::vector<float> a((size_t)(T * K));
+  const int64_t cb = (int64_t)K * act_bits / 8;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint8_t* c = codes + t * cb;
+    float* d = a.data() + t * K;
+    if (act_bits == 8) {
+      for (int k = 0; k < K; ++k) d[k] = (float)(int8_t)c[k];
+    } else {
+      for (int k = 0; k < K; k += 2) {
+        const int lo = c[k / 2] & 0xF, hi = c[k / 2] >> 4;
+        d[k] = (float)(lo >= 8 ? lo - 16 : lo);
+        d[k + 1] = (float)(hi >= 8 ? hi - 16 : hi);
+      }
+    }
+  }
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(1, N / 16));
+  auto run = [&](int64_t n0, int64_t n1) {
+    switch (bits) {
+      case 2: rows_kernel<2>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
+      case 3: rows_kernel<3>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
+      default: rows_kernel<4>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
+    }
+  };
+  if (nt <= 1) {
+    run(0, N);
+    return;
+  }
+  std::vector<std::thread> pool;
+  const int64_t per = (N + nt - 1) / nt;
+  for (int i = 0; i < nt; ++i) {
+    const int64_t n0 = i * per, n1 = std::min<int64_t>(N, n0 + per);
+    if (n0 < n1) pool.emplace_back(run, n0, n1);
+  }
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace cbq

@@ -236,6 +236,22 @@ int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw, i
                          int32_t max_iters, uint8_t* idx, uint16_t* codebook,
                          int32_t* iters_done, void* stream);
 
+/*
+ * cbq_cpu_lut_gemm - the same codebook-LUT GEMM on host cores (x86-64 with AVX2, FMA,
+ * F16C and BMI2).  Passage: CodeQuant abstract (dedicated kernels for GPU and CPU) and the
+ * AI Radio episode, "Improvements" (a CPU speedup from looking products up).
+ *
+ *  All pointers are HOST memory; the call is synchronous and returns when out is
+ *  written.  codes/scales as for cbq_codebook_lut_gemm (row t reads token t);
+ *  W: one weight set (E = 1) with host pointers; out fp32 [T][ldo], ldo >= N.
+ *  out[t][n] = scales[t] * sum_k q[t][k] * C[n][idx(n, k)]: every product is exact in
+ *  fp32, the fp32 summation order differs from the definition.
+ *  n_threads: rows are split over that many threads (0 = all hardware threads).
+ *  CBQ_EUNSUPPORTED when the CPU lacks the instructions.
+ */
+int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits, int64_t T,
+                     const cbq_weights* W, float* out, int64_t ldo, int32_t n_threads);
+
 /* Name of a status code, and the calling thread's message for its last failure. */
 const char* cbq_status_string(int status);
 const char* cbq_last_error(void);
