@@ -279,19 +279,25 @@ def bench_cpu_lut(args, cbq, torch):
         x = datagen.dense_tokens(wl, T)
         rq = oracle.rotate_quantize(x, 0, wl.act_bits)
         out = np.empty((T, wl.N), dtype=np.float32)
-        cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, ws.idx, ws.codebook, ws.K, ws.bits, out=out)
         reps = max(5, args.steps)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, ws.idx, ws.codebook, ws.K, ws.bits, out=out)
-        t_lut = (time.perf_counter() - t0) / reps
+        t_var = {}
+        for name, wide in (("avx2", False), ("avx512", True)):
+            cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, ws.idx, ws.codebook, ws.K, ws.bits,
+                             out=out, avx512=wide)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, ws.idx, ws.codebook, ws.K, ws.bits,
+                                 out=out, avx512=wide)
+            t_var[name] = (time.perf_counter() - t0) / reps
+        t_lut = t_var["avx512"]
         xb = torch.from_numpy(oracle.bf16_bits_to_f64(x).astype(np.float32)).to(torch.bfloat16)
         torch.matmul(xb, W.t())
         t0 = time.perf_counter()
         for _ in range(reps):
             torch.matmul(xb, W.t())
         t_bf16 = (time.perf_counter() - t0) / reps
-        rows[T] = dict(lut_us=round(t_lut * 1e6, 1), bf16_us=round(t_bf16 * 1e6, 1),
+        rows[T] = dict(lut_us=round(t_lut * 1e6, 1), lut_avx2_us=round(t_var["avx2"] * 1e6, 1),
+                       bf16_us=round(t_bf16 * 1e6, 1),
                        speedup_vs_bf16=round(t_bf16 / t_lut, 2),
                        weight_gbs=round(nbytes_w / t_lut / 1e9, 1))
     T = max(wl.T_list)

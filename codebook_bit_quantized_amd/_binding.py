@@ -66,7 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                  i64, vp, sz, vp]),
         "cbq_moe_combine": (ctypes.c_int, [vp, vp, vp, i64, i32, i32, i32, vp, vp]),
         "cbq_kmeans_codebooks": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
-        "cbq_cpu_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, W, vp, i64, i32]),
+        "cbq_cpu_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, W, vp, i64, i32, i32]),
         "cbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "cbq_last_error": (ctypes.c_char_p, []),
         "cbq_version": (ctypes.c_int, []),
@@ -239,8 +239,11 @@ def kmeans_codebooks(w: torch.Tensor, bits: int, max_iters: int = 50, idx: Optio
     return CodebookWeights(idx=idx, codebook=codebook, K=K, bits=bits)
 
 
+CPU_NO_AVX512 = 1
+
+
 def cpu_lut_gemm(codes, scales, act_bits: int, idx, codebook, K: int, bits: int,
-                 n_threads: int = 0, out=None):
+                 n_threads: int = 0, out=None, avx512: bool = True):
     """The LUT GEMM on host cores (cbq_cpu_lut_gemm).  numpy arrays: codes uint8
     [T][K*act_bits/8], scales float32 [T], idx uint8 [N][K*bits/8] (or [1][N][...]),
     codebook uint16 [N][2^bits]; returns float32 [T][N]."""
@@ -256,7 +259,7 @@ def cpu_lut_gemm(codes, scales, act_bits: int, idx, codebook, K: int, bits: int,
     w = cbq_weights(idx.ctypes.data, codebook.ctypes.data, 1, N, K, bits)
     _check(lib.cbq_cpu_lut_gemm(ctypes.c_void_p(codes.ctypes.data), ctypes.c_void_p(scales.ctypes.data),
                                 act_bits, T, ctypes.byref(w), ctypes.c_void_p(out.ctypes.data),
-                                out.strides[0] // 4, n_threads))
+                                out.strides[0] // 4, n_threads, 0 if avx512 else CPU_NO_AVX512))
     return out
 
 

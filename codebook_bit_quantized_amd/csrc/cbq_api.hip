@@ -213,7 +213,7 @@ CBQ_EXPORT int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int
 
 CBQ_EXPORT int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits,
                                 int64_t T, const cbq_weights* W, float* out, int64_t ldo,
-                                int32_t n_threads) {
+                                int32_t n_threads, int32_t flags) {
   g_err[0] = 0;
   if (!W) return fail(CBQ_EINVAL, "W must be non-null");
   if (int rc = check_weights(W, 0)) return rc;
@@ -222,11 +222,12 @@ CBQ_EXPORT int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32
   if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0");
   if (ldo < W->N) return fail(CBQ_EINVAL, "ldo must be >= N");
   if (n_threads < 0) return fail(CBQ_EINVAL, "n_threads must be >= 0");
+  if (flags & ~CBQ_CPU_NO_AVX512) return fail(CBQ_EINVAL, "unknown flags 0x%x", flags);
   if (T == 0) return CBQ_OK;
   if (!codes || !scales || !out) return fail(CBQ_EINVAL, "codes, scales and out must be non-null");
   if (!cbq::cpu_lut_supported()) return fail(CBQ_EUNSUPPORTED, "the CPU kernel needs AVX2, FMA, F16C and BMI2");
   cbq::cpu_lut_gemm_impl(codes, scales, act_bits, T, W->N, W->K, W->bits, W->idx, W->codebook, out,
-                         ldo, n_threads);
+                         ldo, n_threads, (flags & CBQ_CPU_NO_AVX512) == 0);
   return CBQ_OK;
 }
 

@@ -10,7 +10,8 @@
 // dequantised once per row and reused by up to 8 tokens held in registers.
 //
 // Index unpacking: 4-bit nibbles with byte shuffles; 3- and 2-bit fields with BMI2
-// pdep (eight indices per 24 or 16 bits).
+// pdep (eight indices per 24 or 16 bits).  On CPUs with AVX-512 a second variant
+// looks 16 weights up per vpermps in an fp32 copy of the row's codebook.
 #include "cpu_lut.hpp"
 
 #include <immintrin.h>
@@ -124,11 +125,84 @@ void rows_kernel(const float* a, const float* scales, int64_t T, int64_t n0, int
   }
 }
 
+// AVX-512 variant: the codebook is widened once per row into an fp32 table of 16
+// lanes, and vpermps looks up 16 weights per instruction, already as fp32.  Indices
+// are spread into bytes with pdep, then zero-extended to 16 dwords.
+template <int BITS>
+__attribute__((target("avx512f,bmi2"))) inline __m512i load_indices16(const uint8_t* row, int k) {
+  constexpr uint64_t MASK = BITS == 4 ? 0x0F0F0F0F0F0F0F0Full
+                          : BITS == 3 ? 0x0707070707070707ull : 0x0303030303030303ull;
+  constexpr int GB = BITS;                                  // bytes per 8 indices
+  const uint8_t* p = row + (int64_t)k * BITS / 8;
+  uint64_t f0 = 0, f1 = 0;
+  for (int b = 0; b < GB; ++b) {
+    f0 |= (uint64_t)p[b] << (8 * b);
+    f1 |= (uint64_t)p[GB + b] << (8 * b);
+  }
+  const __m128i bytes = _mm_set_epi64x((long long)_pdep_u64(f1, MASK), (long long)_pdep_u64(f0, MASK));
+  return _mm512_cvtepu8_epi32(bytes);
+}
+
+template <int BITS, int TB>
+__attribute__((target("avx512f,bmi2")))
+inline void row_tokens512(const float* a, const float* scales, int64_t t0, int K, const uint8_t* row,
+                          __m512 tab, float* out, int64_t ldo, int64_t n) {
+  constexpr int NA = TB <= 2 ? 4 : (TB <= 4 ? 2 : 1);
+  __m512 acc[TB][NA];
+#pragma GCC unroll 8
+  for (int t = 0; t < TB; ++t)
+#pragma GCC unroll 4
+    for (int q = 0; q < NA; ++q) acc[t][q] = _mm512_setzero_ps();
+  for (int k = 0; k < K; k += 32) {
+    const __m512 w0 = _mm512_permutexvar_ps(load_indices16<BITS>(row, k), tab);
+    const __m512 w1 = _mm512_permutexvar_ps(load_indices16<BITS>(row, k + 16), tab);
+#pragma GCC unroll 8
+    for (int t = 0; t < TB; ++t) {
+      const float* at = a + (t0 + t) * (int64_t)K + k;
+      acc[t][0] = _mm512_fmadd_ps(w0, _mm512_loadu_ps(at), acc[t][0]);
+      acc[t][1 % NA] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(at + 16), acc[t][1 % NA]);
+    }
+  }
+#pragma GCC unroll 8
+  for (int t = 0; t < TB; ++t) {
+    __m512 v = acc[t][0];
+#pragma GCC unroll 4
+    for (int q = 1; q < NA; ++q) v = _mm512_add_ps(v, acc[t][q]);
+    out[(t0 + t) * ldo + n] = scales[t0 + t] * _mm512_reduce_add_ps(v);
+  }
+}
+
+template <int BITS>
+__attribute__((target("avx512f,bmi2,f16c")))
+void rows_kernel512(const float* a, const float* scales, int64_t T, int64_t n0, int64_t n1, int K,
+                    const uint8_t* idx, const uint16_t* codebook, float* out, int64_t ldo) {
+  constexpr int L = 1 << BITS;
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  for (int64_t n = n0; n < n1; ++n) {
+    alignas(64) float ctab[16] = {0};
+    for (int c = 0; c < L; ++c) ctab[c] = _cvtsh_ss(codebook[n * L + c]);
+    const __m512 tab = _mm512_load_ps(ctab);
+    const uint8_t* row = idx + n * row_bytes;
+    int64_t t0 = 0;
+    for (; t0 + 8 <= T; t0 += 8) row_tokens512<BITS, 8>(a, scales, t0, K, row, tab, out, ldo, n);
+    switch (T - t0) {
+      case 1: row_tokens512<BITS, 1>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 2: row_tokens512<BITS, 2>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 3: row_tokens512<BITS, 3>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 4: row_tokens512<BITS, 4>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 5: row_tokens512<BITS, 5>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 6: row_tokens512<BITS, 6>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 7: row_tokens512<BITS, 7>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      default: break;
+    }
+  }
+}
+
 }  // namespace
 
 void cpu_lut_gemm_impl(const uint8_t* codes, const float* scales, int act_bits, int64_t T,
                        int64_t N, int K, int bits, const uint8_t* idx, const uint16_t* codebook,
-                       float* out, int64_t ldo, int n_threads) {
+                       float* out, int64_t ldo, int n_threads, bool use_avx512) {
   // activation codes -> fp32 (exact small integers), natural channel order
   std::vector<float> a((size_t)(T * K));
   const int64_t cb = (int64_t)K * act_bits / 8;
@@ -147,7 +221,16 @@ void cpu_lut_gemm_impl(const uint8_t* codes, const float* scales, int act_bits, 
   }
   int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
   nt = (int)std::min<int64_t>(nt, std::max<int64_t>(1, N / 16));
+  const bool wide = use_avx512 && __builtin_cpu_supports("avx512f");
   auto run = [&](int64_t n0, int64_t n1) {
+    if (wide) {
+      switch (bits) {
+        case 2: rows_kernel512<2>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
+        case 3: rows_kernel512<3>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
+        default: rows_kernel512<4>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
+      }
+      return;
+    }
     switch (bits) {
       case 2: rows_kernel<2>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;
       case 3: rows_kernel<3>(a.data(), scales, T, n0, n1, K, idx, codebook, out, ldo); break;

@@ -247,10 +247,14 @@ int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw, i
  *  out[t][n] = scales[t] * sum_k q[t][k] * C[n][idx(n, k)]: every product is exact in
  *  fp32, the fp32 summation order differs from the definition.
  *  n_threads: rows are split over that many threads (0 = all hardware threads).
+ *  flags: 0, or CBQ_CPU_NO_AVX512 to keep to the AVX2 kernel on a CPU with AVX-512F
+ *  (which otherwise gets a variant looking up 16 fp32 centroids per instruction).
  *  CBQ_EUNSUPPORTED when the CPU lacks the instructions.
  */
+#define CBQ_CPU_NO_AVX512 1
 int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits, int64_t T,
-                     const cbq_weights* W, float* out, int64_t ldo, int32_t n_threads);
+                     const cbq_weights* W, float* out, int64_t ldo, int32_t n_threads,
+                     int32_t flags);
 
 /* Name of a status code, and the calling thread's message for its last failure. */
 const char* cbq_status_string(int status);

@@ -38,9 +38,11 @@ def _normwise(y, ref):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("act_bits", [4, 8])
 @pytest.mark.parametrize("T", [1, 5, 8, 19])
-def test_cpu_lut_matches_oracle(bits, act_bits, T):
+@pytest.mark.parametrize("avx512", [False, True])
+def test_cpu_lut_matches_oracle(bits, act_bits, T, avx512):
     ws, rq, ref = _case(100 + bits * 10 + T, T, 80, 288, bits, act_bits)
-    y = cbq.cpu_lut_gemm(rq["codes"], rq["scale"], act_bits, ws.idx, ws.codebook, ws.K, bits)
+    y = cbq.cpu_lut_gemm(rq["codes"], rq["scale"], act_bits, ws.idx, ws.codebook, ws.K, bits,
+                         avx512=avx512)
     assert _normwise(y, ref) <= 1e-3
 
 
@@ -62,8 +64,9 @@ def test_cpu_lut_identity_codebook_layout():
         cb[:, 1] = 0x3C00                                   # fp16 1.0
         x = datagen.random_tokens(3, 4, K)
         rq = oracle.rotate_quantize(x, 0, 4)
-        y = cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, idx, cb, K, bits)
-        assert np.array_equal(y, (rq["q"].astype(np.float32) * rq["scale"][:, None]).astype(np.float32))
+        for avx512 in (False, True):
+            y = cbq.cpu_lut_gemm(rq["codes"], rq["scale"], 4, idx, cb, K, bits, avx512=avx512)
+            assert np.array_equal(y, (rq["q"].astype(np.float32) * rq["scale"][:, None]).astype(np.float32))
 
 
 def test_cpu_lut_dense_decode_linear():
@@ -81,8 +84,9 @@ def test_cpu_lut_validation():
     import ctypes
     lib = cbq.load_library()
     w = cbq.cbq_weights(0x1000, 0x2000, 2, 64, 256, 4)       # E = 2: one weight set only
-    assert lib.cbq_cpu_lut_gemm(None, None, 4, 4, ctypes.byref(w), None, 64, 0) == cbq.CBQ_EUNSUPPORTED
+    assert lib.cbq_cpu_lut_gemm(None, None, 4, 4, ctypes.byref(w), None, 64, 0, 0) == cbq.CBQ_EUNSUPPORTED
     w = cbq.cbq_weights(0x1000, 0x2000, 1, 64, 256, 4)
-    assert lib.cbq_cpu_lut_gemm(None, None, 4, 0, ctypes.byref(w), None, 64, 0) == cbq.CBQ_OK
-    assert lib.cbq_cpu_lut_gemm(None, None, 4, 4, ctypes.byref(w), None, 64, 0) == cbq.CBQ_EINVAL
-    assert lib.cbq_cpu_lut_gemm(None, None, 6, 4, ctypes.byref(w), None, 64, 0) == cbq.CBQ_EINVAL
+    assert lib.cbq_cpu_lut_gemm(None, None, 4, 0, ctypes.byref(w), None, 64, 0, 0) == cbq.CBQ_OK
+    assert lib.cbq_cpu_lut_gemm(None, None, 4, 4, ctypes.byref(w), None, 64, 0, 0) == cbq.CBQ_EINVAL
+    assert lib.cbq_cpu_lut_gemm(None, None, 6, 4, ctypes.byref(w), None, 64, 0, 0) == cbq.CBQ_EINVAL
+    assert lib.cbq_cpu_lut_gemm(None, None, 4, 0, ctypes.byref(w), None, 64, 0, 2) == cbq.CBQ_EINVAL
