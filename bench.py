@@ -265,12 +265,12 @@ def bench_cpu_lut(args, cbq, torch):
     wl = datagen.WORKLOADS["dense2560x9728"]
     ws = datagen.dense_weights(wl, "gate_up")
     nbytes_w = ws.idx.nbytes + ws.codebook.nbytes
-    big = np.ones(1 << 28, dtype=np.float32)                  # 1 GiB
+    big = torch.ones(1 << 28, dtype=torch.float32)            # 1 GiB, summed by all host threads
     big.sum()
     t0 = time.perf_counter()
-    for _ in range(3):
+    for _ in range(5):
         big.sum()
-    stream_gbs = 3 * big.nbytes / (time.perf_counter() - t0) / 1e9
+    stream_gbs = 5 * big.numel() * 4 / (time.perf_counter() - t0) / 1e9
     del big
     W = torch.from_numpy(oracle.dequantize(oracle.unpack_indices(ws.idx[0], ws.K, ws.bits),
                                            ws.codebook[0]).astype(np.float32)).to(torch.bfloat16)
@@ -301,7 +301,6 @@ def bench_cpu_lut(args, cbq, torch):
                        speedup_vs_bf16=round(t_bf16 / t_lut, 2),
                        weight_gbs=round(nbytes_w / t_lut / 1e9, 1))
     T = max(wl.T_list)
-    t_lut = rows[T]["lut_us"] / 1e6
     cpu = None
     if not args.no_cpu_baseline:
         x = datagen.dense_tokens(wl, T)
@@ -313,17 +312,121 @@ def bench_cpu_lut(args, cbq, torch):
         cpu = dict(value=round(T / dt, 2), unit="tokens/s", cores=1, kind="oracle",
                    sample=f"oracle rotate+quantise and dequantise-then-matmul of the 2560->9728 "
                           f"linear for {T} tokens ({dt:.2f} s, numpy fp64)")
+    # tokens/s over one pass of every batch size; roofline of the single-token GEMV
+    t_all = sum(r["lut_us"] for r in rows.values()) / 1e6
+    tokens = sum(wl.T_list)
+    t_lut = rows[min(wl.T_list)]["lut_us"] / 1e6
     gbs = nbytes_w / t_lut / 1e9
-    line = dict(metric="CPU LUT GEMM tokens/s", value=round(T / t_lut, 1), unit="tokens/s",
-                n_gpus=0, steps=max(5, args.steps), warmup=1, ms_per_step=round(t_lut * 1e3, 4),
+    line = dict(metric="CPU LUT GEMM tokens/s", value=round(tokens / t_all, 1), unit="tokens/s",
+                n_gpus=0, steps=max(5, args.steps), warmup=1, ms_per_step=round(t_all * 1e3, 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
                 config=dict(workload="cpu_lut_dense2560x9728", K=wl.K, N=wl.N, bits=wl.bits,
                             act_bits=wl.act_bits, host_threads=os.cpu_count(), per_batch=rows),
                 roofline=dict(bound="dram", achieved=round(gbs, 1), peak=round(stream_gbs, 1),
                               unit="GB/s", frac=round(gbs / stream_gbs, 4), traffic=None,
-                              kernel="cpu_lut_gemm (weights once per call)",
-                              peak_note="host streaming read rate measured in this run"),
+                              kernel="cpu_lut_gemm, 1 token (weights once per call)",
+                              peak_note="host streaming read rate (all threads) measured in this run"),
                 cpu_baseline=cpu, host=platform.node())
+    print(json.dumps(line))
+
+
+def bench_latency_table(args, cbq, torch):
+    """Adaptive cluster allocation on the 64 + 2 expert layer: the decode GEMMs timed
+    (caches flushed) with every matrix at 2, 3 and 4 bits give the latency per matrix
+    and width; a synthetic importance (the expert's share of the routed prefill tokens,
+    times the K-means clustering error of synthetic bf16 weights at that width, built on
+    the GPU) gives the error; the allocation minimises the summed error within the
+    latency of a uniform 3-bit layer."""
+    from codebook_bit_quantized_amd.allocation import allocate_bits, clustering_error
+    import oracle
+    wl = datagen.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    E = wl.E + wl.n_shared
+    choices = (2, 3, 4)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def cold(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e) * 1000.0)
+        return float(np.median(ts))
+
+    xd, lgd = datagen.moe_tokens(wl, 32, decode=True)
+    xdt = torch.from_numpy(xd.view(np.int16)).to(dev).view(torch.bfloat16)
+    codes, scales = cbq.rotate_quantize(xdt, wl.act_bits)
+    rt = cbq.moe_route_gather(torch.from_numpy(lgd).to(dev), wl.topk, True, wl.n_shared)
+    R = rt["sorted_tokens"].shape[0]
+    h = torch.empty((R, wl.F), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((R, wl.H), dtype=torch.float32, device=dev)
+
+    def upw(ws):
+        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
+                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
+                                   K=ws.K, bits=ws.bits)
+
+    table = {}
+    for bits in choices:
+        G = upw(datagen.weight_set(wl.wid, datagen.TAG_GATE_IDX, datagen.TAG_GATE_CB, E, wl.F, wl.H, bits))
+        U = upw(datagen.weight_set(wl.wid, datagen.TAG_UP_IDX, datagen.TAG_UP_CB, E, wl.F, wl.H, bits))
+        D = upw(datagen.weight_set(wl.wid, datagen.TAG_DOWN_IDX, datagen.TAG_DOWN_CB, E, wl.H, wl.F, bits))
+        gu = cold(lambda: cbq.codebook_lut_gemm(codes, scales, wl.act_bits, [G, U],
+                                                expert_offsets=rt["offsets"],
+                                                row_token=rt["sorted_tokens"], path=cbq.PATH_LUT, out=h))
+        ch, sh = cbq.rotate_quantize(h, wl.act_bits)
+        dn = cold(lambda: cbq.codebook_lut_gemm(ch, sh, wl.act_bits, [D], expert_offsets=rt["offsets"],
+                                                path=cbq.PATH_LUT, out=out))
+        table[bits] = dict(decode_gate_up_us=round(gu, 2), decode_down_us=round(dn, 2))
+        del G, U, D
+    del flush
+
+    # importance: share of the routed prefill tokens per expert (shared experts: all)
+    xp, lgp = datagen.moe_tokens(wl, wl.T_list[0])
+    counts = oracle.route(lgp, wl.topk, True, wl.n_shared)["counts"].astype(np.float64)
+    share = np.concatenate([counts / wl.T_list[0], np.ones(wl.n_shared)])
+    # clustering error per matrix and width on a sample of synthetic bf16 weight rows
+    rows = 64
+    kinds = (("gate", wl.F, wl.H), ("up", wl.F, wl.H), ("down", wl.H, wl.F))
+    err = np.zeros((E * 3, len(choices)))
+    lat = np.zeros((E * 3, len(choices)))
+    for m, (name, N, K) in enumerate(kinds):
+        w_np = np.concatenate([datagen.weights_bf16(wl.wid, datagen.TAG_W_FULL, 3 * e + m, rows, K)
+                               for e in range(E)])
+        wf = oracle.bf16_bits_to_f64(w_np)
+        w = torch.from_numpy(w_np.view(np.int16)).to(dev)
+        for c, bits in enumerate(choices):
+            cw = cbq.kmeans_codebooks(w, bits, 30)
+            idx = oracle.unpack_indices(cw.idx[0].cpu().numpy(), K, bits)
+            cbk = oracle.f16_bits_to_f64(cw.codebook[0].cpu().numpy().view(np.uint16))
+            for e in range(E):
+                sl = slice(e * rows, (e + 1) * rows)
+                err[3 * e + m, c] = share[e] * clustering_error(wf[sl], cbk[sl], idx[sl]) * (N / rows)
+            key = "decode_down_us" if name == "down" else "decode_gate_up_us"
+            lat[3 * np.arange(E) + m, c] = table[bits][key] / E / (1 if name == "down" else 2)
+    budget = float(lat[:, 1].sum()) * 1.01      # a uniform 3-bit layer (+1 %: latency grid slack)
+    bits = allocate_bits(lat, err, budget)
+    pick = bits - 2
+    res = dict(uniform3_error=float(err[:, 1].sum()),
+               allocated_error=float(err[np.arange(len(bits)), pick].sum()),
+               budget_us=round(budget, 2),
+               allocated_latency_us=round(float(lat[np.arange(len(bits)), pick].sum()), 2),
+               bits_histogram={str(b): int((bits == b).sum()) for b in choices},
+               shared_expert_bits=[int(b) for b in bits[3 * wl.E:]])
+    line = dict(metric="cluster allocation at equal decode latency", value=round(
+                    res["uniform3_error"] / max(res["allocated_error"], 1e-30), 4),
+                unit="error reduction vs uniform 3-bit (x)", n_gpus=1, steps=10, warmup=1,
+                ms_per_step=None, higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="f16", data="synthetic",
+                config=dict(workload=f"allocation_{wl.name}", latency_table_us=table,
+                            matrices=E * 3, sample_rows=rows),
+                roofline=None, cpu_baseline=None, allocation=res, host=platform.node())
     print(json.dumps(line))
 
 
@@ -388,6 +491,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=20)
     ap.add_argument("--cpu-lut", action="store_true",
                     help="measure the host (CPU) LUT GEMM on the dense decode linear instead")
+    ap.add_argument("--latency-table", action="store_true",
+                    help="measure GEMM latency per codebook width and run the cluster allocation")
     ap.add_argument("--kmeans", action="store_true",
                     help="measure offline codebook construction (per-row K-means) instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -424,6 +529,9 @@ def main():
 
     if args.kmeans:
         bench_kmeans(args, cbq, torch)
+        return
+    if args.latency_table:
+        bench_latency_table(args, cbq, torch)
         return
 
     wl = datagen.WORKLOADS[args.workload]

@@ -143,27 +143,28 @@ __attribute__((target("avx512f,bmi2"))) inline __m512i load_indices16(const uint
   return _mm512_cvtepu8_epi32(bytes);
 }
 
+// TB <= 16 tokens: their accumulators fit the 32 vector registers with the weights.
 template <int BITS, int TB>
 __attribute__((target("avx512f,bmi2")))
 inline void row_tokens512(const float* a, const float* scales, int64_t t0, int K, const uint8_t* row,
                           __m512 tab, float* out, int64_t ldo, int64_t n) {
   constexpr int NA = TB <= 2 ? 4 : (TB <= 4 ? 2 : 1);
   __m512 acc[TB][NA];
-#pragma GCC unroll 8
+#pragma GCC unroll 16
   for (int t = 0; t < TB; ++t)
 #pragma GCC unroll 4
     for (int q = 0; q < NA; ++q) acc[t][q] = _mm512_setzero_ps();
   for (int k = 0; k < K; k += 32) {
     const __m512 w0 = _mm512_permutexvar_ps(load_indices16<BITS>(row, k), tab);
     const __m512 w1 = _mm512_permutexvar_ps(load_indices16<BITS>(row, k + 16), tab);
-#pragma GCC unroll 8
+#pragma GCC unroll 16
     for (int t = 0; t < TB; ++t) {
       const float* at = a + (t0 + t) * (int64_t)K + k;
       acc[t][0] = _mm512_fmadd_ps(w0, _mm512_loadu_ps(at), acc[t][0]);
       acc[t][1 % NA] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(at + 16), acc[t][1 % NA]);
     }
   }
-#pragma GCC unroll 8
+#pragma GCC unroll 16
   for (int t = 0; t < TB; ++t) {
     __m512 v = acc[t][0];
 #pragma GCC unroll 4
@@ -184,7 +185,7 @@ void rows_kernel512(const float* a, const float* scales, int64_t T, int64_t n0, 
     const __m512 tab = _mm512_load_ps(ctab);
     const uint8_t* row = idx + n * row_bytes;
     int64_t t0 = 0;
-    for (; t0 + 8 <= T; t0 += 8) row_tokens512<BITS, 8>(a, scales, t0, K, row, tab, out, ldo, n);
+    for (; t0 + 16 <= T; t0 += 16) row_tokens512<BITS, 16>(a, scales, t0, K, row, tab, out, ldo, n);
     switch (T - t0) {
       case 1: row_tokens512<BITS, 1>(a, scales, t0, K, row, tab, out, ldo, n); break;
       case 2: row_tokens512<BITS, 2>(a, scales, t0, K, row, tab, out, ldo, n); break;
@@ -193,6 +194,14 @@ void rows_kernel512(const float* a, const float* scales, int64_t T, int64_t n0, 
       case 5: row_tokens512<BITS, 5>(a, scales, t0, K, row, tab, out, ldo, n); break;
       case 6: row_tokens512<BITS, 6>(a, scales, t0, K, row, tab, out, ldo, n); break;
       case 7: row_tokens512<BITS, 7>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 8: row_tokens512<BITS, 8>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 9: row_tokens512<BITS, 9>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 10: row_tokens512<BITS, 10>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 11: row_tokens512<BITS, 11>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 12: row_tokens512<BITS, 12>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 13: row_tokens512<BITS, 13>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 14: row_tokens512<BITS, 14>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 15: row_tokens512<BITS, 15>(a, scales, t0, K, row, tab, out, ldo, n); break;
       default: break;
     }
   }

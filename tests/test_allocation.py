@@ -1,0 +1,58 @@
+"""Adaptive cluster allocation (CodeQuant2, Figure 3 left): the dynamic programme is
+checked against exhaustive search on small instances, and for the properties any
+optimum has (budget respected, error non-increasing as the budget grows)."""
+import itertools
+
+import numpy as np
+import pytest
+
+from codebook_bit_quantized_amd.allocation import allocate_bits
+
+
+def _brute(lat, err, budget, grid):
+    unit = budget / grid
+    cost = np.ceil(lat / unit - 1e-9)
+    best, arg = np.inf, None
+    for combo in itertools.product(range(lat.shape[1]), repeat=lat.shape[0]):
+        c = sum(cost[i, j] for i, j in enumerate(combo))
+        e = sum(err[i, j] for i, j in enumerate(combo))
+        if c <= grid and e < best - 1e-12:
+            best, arg = e, combo
+    return best, arg
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_dp_matches_exhaustive_search(seed):
+    g = np.random.default_rng(seed)
+    M = 6
+    lat = np.sort(g.uniform(1, 10, (M, 3)), axis=1)          # more bits: slower
+    err = -np.sort(-g.uniform(0, 5, (M, 3)), axis=1)         # more bits: less error
+    budget = float(lat.mean(axis=1).sum())
+    bits = allocate_bits(lat, err, budget, grid=400)
+    chosen = bits - 2
+    e = err[np.arange(M), chosen].sum()
+    best, _ = _brute(lat, err, budget, 400)
+    assert e == pytest.approx(best, abs=1e-12)
+    assert lat[np.arange(M), chosen].sum() <= budget + 1e-9
+
+
+def test_more_budget_never_more_error():
+    g = np.random.default_rng(11)
+    M = 30
+    lat = np.sort(g.uniform(1, 10, (M, 3)), axis=1)
+    err = -np.sort(-g.uniform(0, 5, (M, 3)), axis=1)
+    lo, hi = lat[:, 0].sum(), lat[:, 2].sum()
+    prev = np.inf
+    for f in np.linspace(0.05, 1, 9):   # the grid rounds latencies up: start above the minimum
+        budget = lo + f * (hi - lo) + 1e-6
+        bits = allocate_bits(lat, err, budget)
+        e = err[np.arange(M), bits - 2].sum()
+        assert e <= prev + 1e-9
+        prev = e
+    assert np.all(allocate_bits(lat, err, hi * 1.01) == 4)   # everything fits (grid slack < 1%)
+
+
+def test_budget_below_fastest_raises():
+    lat = np.array([[1.0, 2.0, 3.0]])
+    with pytest.raises(ValueError):
+        allocate_bits(lat, np.zeros((1, 3)), 0.5)
