@@ -102,10 +102,40 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   // (with the activation conversion and the first matrix's dequantisation); sub-step
   // 3 runs after it from fragments already in registers, so the next step's first
   // fragment reads (which need the barrier) overlap MFMAs instead of stalling.
+  // Piece j (0..3) of one lane's 32-index dequantisation: indices 8j..8j+7.
+  auto dq_piece = [&](const RowTable<BITS>& t, const uint32_t (&w)[BITS], uint32_t* d, int j) {
+    if constexpr (BITS == 4) {
+      dequant4(t, w[j], d + 4 * j);
+    } else if constexpr (BITS == 3) {
+      const uint32_t f = j == 0 ? w[0] : j == 1 ? __builtin_amdgcn_alignbit(w[1], w[0], 24)
+                       : j == 2 ? __builtin_amdgcn_alignbit(w[2], w[1], 16) : (w[2] >> 8);
+      dequant3(t, f, d + 4 * j);
+    } else {
+      uint32_t tmp[8];
+      dequant2(t, w[j >> 1], tmp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[4 * j + i] = tmp[4 * (j & 1) + i];
+    }
+  };
+  // Piece p (0..7) of the activation conversion: codes 8p..8p+7 -> one 16-byte LDS store.
+  auto a_piece = [&](int buf, const uint32_t* a, int p) {
+    uint32_t d[4];
+    const int h = p >> 2, j = p & 3;
+    if constexpr (ABITS == 4) codes4_to_f16(a[h * 4 + j], d);
+    else codes8_to_f16(a[h * 8 + 2 * j], a[h * 8 + 2 * j + 1], d);
+    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][tid * LDW]);
+    ap[p] = u32x4{d[0], d[1], d[2], d[3]};
+  };
+  // One step: MFMAs on LDS buffer `buf` with weights `bd`, while step kt+1 is
+  // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
+  // (wf, af_raw) is refilled with step kt+2.  The preparation is cut into pieces that
+  // are placed between the MFMA pairs in program order (scheduling fences keep them
+  // there), so the vector ALU work issues while the matrix cores are busy.
   auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
                   uint32_t (&wn)[2][BITS], uint32_t* an, uint32_t (&wf)[2][BITS], uint32_t* af_raw) {
     gload(kt + 2, wf, af_raw);
-    __builtin_amdgcn_sched_barrier(0);        // keep the refill at the top of the step
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int PRE = 3 * NMS;     // MFMA pairs before the barrier
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
       const f16x8 b0 = as_f16x8(bd[0][4 * kk], bd[0][4 * kk + 1], bd[0][4 * kk + 2], bd[0][4 * kk + 3]);
@@ -115,19 +145,15 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
         acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
         acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
         af[ms] = frag(buf, kk + 1, ms);
+        const int i = kk * NMS + ms;
+#pragma unroll
+        for (int p = (12 * i + PRE - 1) / PRE; p < (12 * (i + 1) + PRE - 1) / PRE; ++p) {
+          if (p < 8) a_piece(buf ^ 1, an, p);
+          else dq_piece(c.tab[0], wn[0], bn[0], p - 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    astore(buf ^ 1, an);
-    dequant32<BITS>(c.tab[0], wn[0], bn[0]);
-#pragma unroll
-    for (int i = 0; i < 6 * NMS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     {
       const f16x8 b0 = as_f16x8(bd[0][12], bd[0][13], bd[0][14], bd[0][15]);
@@ -137,16 +163,12 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
         acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
         acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
         af[ms] = frag(buf ^ 1, 0, ms);
+#pragma unroll
+        for (int p = (4 * ms + NMS - 1) / NMS; p < (4 * (ms + 1) + NMS - 1) / NMS; ++p)
+          dq_piece(c.tab[1], wn[1], bn[1], p);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    dequant32<BITS>(c.tab[1], wn[1], bn[1]);
-#pragma unroll
-    for (int i = 0; i < 2 * NMS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   gload(0, rw[0], ra[0]);
