@@ -50,6 +50,27 @@ KERNEL_SOURCES = {
 }
 
 
+class CacheFlush:
+    """Evicts L2 and the MALL (256 MB) before a cold measurement.
+
+    mode "read" sums a 1 GiB buffer, leaving the caches full of clean lines.  Mode
+    "write" fills it instead: that also evicts everything, but leaves up to the MALL's
+    size of dirty lines whose write-back then lands inside the measured kernel and
+    roughly halves the read bandwidth it sees.
+    """
+
+    def __init__(self, torch, dev, mode="read"):
+        self.mode = mode
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.buf.sum()
+
+    def __call__(self):
+        if self.mode == "write":
+            self.buf.fill_(1.0)
+        else:
+            self.buf.sum()
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -343,14 +364,14 @@ def bench_latency_table(args, cbq, torch):
     dev = "cuda:0"
     E = wl.E + wl.n_shared
     choices = (2, 3, 4)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = CacheFlush(torch, dev, args.flush)
 
     def cold(fn, reps=10):
         fn()
         torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
-            flush.fill_(1.0)
+            flush()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
             fn()
@@ -489,6 +510,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefill-sample", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--flush", choices=("read", "write"), default="read",
+                    help="how caches are emptied before cold GEMM timings (see CacheFlush)")
     ap.add_argument("--cpu-lut", action="store_true",
                     help="measure the host (CPU) LUT GEMM on the dense decode linear instead")
     ap.add_argument("--latency-table", action="store_true",
@@ -596,12 +619,12 @@ def main():
     dom_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(start_evs, end_evs)]))
 
     def cold_gemm_ms(p):
-        """Median duration of p's gate/up GEMM with the caches flushed (1 GiB written,
-        more than L2 + MALL) before every repetition."""
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        """Median duration of p's gate/up GEMM with L2 and the MALL flushed before every
+        repetition (by default by reading 1 GiB)."""
+        flush = CacheFlush(torch, dev, args.flush)
         times = []
         for _ in range(args.decode_reps):
-            flush.fill_(1.0)
+            flush()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
             p.gemm_gu_only()
@@ -623,7 +646,8 @@ def main():
         return dict(tokens=p.T, bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
                     traffic=read_traffic("lut_decode", wl.name), kernel=label,
-                    avg_launch_us=round(d_ms * 1000.0, 2), algorithmic_bytes=d_bytes, **extra)
+                    avg_launch_us=round(d_ms * 1000.0, 2), algorithmic_bytes=d_bytes,
+                    cache_flush=args.flush, **extra)
 
     decode_info = None
     if wl.kind == "moe" and dom.path_gu == cbq.PATH_MFMA:
