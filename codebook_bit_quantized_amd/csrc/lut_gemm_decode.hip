@@ -48,13 +48,13 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t* 
   }
 }
 
-template <int BITS, int ABITS, int NW, int MSUB>
-__global__ void __launch_bounds__(NW == 2 ? 512 : 1024)
+template <int BITS, int ABITS, int NW, int MSUB, int NG>
+__global__ void __launch_bounds__(NW == 2 ? 512 : 1024, BITS <= 3 ? 4 : 3)
 lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                   GemmW w0, GemmW w1, int64_t n_rows, int N, int K, int splitk, int max_rows,
                   void* __restrict__ out, int64_t ldo) {
-  extern __shared__ f32x4 red[];   // [(splitk-1) * NW * MSUB][64]
+  extern __shared__ f32x4 red[];   // [(splitk-1) * NG * NW * MSUB][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = blockIdx.y;
@@ -69,22 +69,27 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   if (me <= 0 || (max_rows >= 0 && me > max_rows)) return;
 
   const int nl = lane & 15, g = lane >> 4;
-  const int n = blockIdx.x * 16 + nl;
-  const bool nvalid = n < N;
-  const int nn = nvalid ? n : 0;
   constexpr int L = 1 << BITS;
   const int64_t row_bytes = (int64_t)K * BITS / 8;
   const int64_t code_bytes = (int64_t)K * ABITS / 8;
-  (void)L;
 
-  RowTable<BITS> tab[NW];
+  // row group q of this workgroup: rows (blockIdx.x * NG + q) * 16 + 0..15
+  int nrow[NG];
+  bool nvalid[NG];
+  uint32_t wlane[NG];
+  RowTable<BITS> tab[NG][NW];
   __amdgpu_buffer_rsrc_t wres[NW];
-  const uint32_t wlane = nvalid ? (uint32_t)(n * row_bytes) + (uint32_t)(g * 4 * BITS) : kOffNone;
-  tab[0].load(w0.codebook + ((int64_t)e * N + nn) * L);
   wres[0] = make_rsrc(w0.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
-  if constexpr (NW == 2) {
-    tab[1].load(w1.codebook + ((int64_t)e * N + nn) * L);
-    wres[1] = make_rsrc(w1.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
+  if constexpr (NW == 2) wres[1] = make_rsrc(w1.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int n = (blockIdx.x * NG + q) * 16 + nl;
+    nrow[q] = n;
+    nvalid[q] = n < N;
+    const int nn = nvalid[q] ? n : 0;
+    wlane[q] = nvalid[q] ? (uint32_t)(n * row_bytes) + (uint32_t)(g * 4 * BITS) : kOffNone;
+    tab[q][0].load(w0.codebook + ((int64_t)e * N + nn) * L);
+    if constexpr (NW == 2) tab[q][1].load(w1.codebook + ((int64_t)e * N + nn) * L);
   }
   const __amdgpu_buffer_rsrc_t cres = make_rsrc(codes, 0x7FFFFFFFu);
 
@@ -98,12 +103,14 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   const int64_t mb_step = rowsplit ? (int64_t)splitk * 16 * MSUB : 16 * MSUB;
 
   for (int64_t mb = mb_first; mb < me; mb += mb_step) {
-    f32x4 acc[NW][MSUB];
+    f32x4 acc[NG][NW][MSUB];
     uint32_t aoff[MSUB];     // byte offset of this lane's activation row per sub-tile
 #pragma unroll
     for (int s = 0; s < MSUB; ++s) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc[w][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc[q][w][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const int64_t m = mb + s * 16 + nl;
       uint32_t o = kOffNone;
       if (m < me) {
@@ -117,15 +124,17 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
 
     // ring of two chunks of raw data, loaded two chunks ahead
     struct Slot {
-      uint32_t w[NW][BITS];
+      uint32_t w[NG][NW][BITS];
       uint32_t a[MSUB][ABITS];
     };
     Slot ring[2];
     auto load = [&](int c, Slot& d) {
       const bool ok = c < c_end && c * 128 + g * 32 < K;
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-        buf_load<4 * BITS>(wres[w], ok ? wlane : kOffNone, d.w[w], (uint32_t)(c * 128 * BITS / 8));
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+          buf_load<4 * BITS>(wres[w], ok ? wlane[q] : kOffNone, d.w[q][w], (uint32_t)(c * 128 * BITS / 8));
       const uint32_t cs = (uint32_t)(c * 128 * ABITS / 8);
 #pragma unroll
       for (int s = 0; s < MSUB; ++s) {
@@ -134,22 +143,50 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
           buf_load<16>(cres, ok ? aoff[s] + 16 * h : kOffNone, &d.a[s][4 * h], cs);
       }
     };
+    // the activation fragments are converted once per chunk and shared by the row groups
     auto chunk = [&](const Slot& cur) {
-      uint32_t bd[NW][16];
+      if constexpr (NG == 1) {
+        // one row group: convert each token sub-tile just before its MFMAs
+        uint32_t bd[NW][16];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[w], cur.w[w], bd[w]);
+        for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[0][w], cur.w[0][w], bd[w]);
 #pragma unroll
-      for (int s = 0; s < MSUB; ++s) {
-        if (s >= nsub) break;
-        uint32_t ad[16];
-        codes32_to_f16<ABITS>(cur.a[s], ad);
+        for (int s = 0; s < MSUB; ++s) {
+          if (s >= nsub) break;
+          uint32_t ad[16];
+          codes32_to_f16<ABITS>(cur.a[s], ad);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x8 A = as_f16x8(ad[4 * j], ad[4 * j + 1], ad[4 * j + 2], ad[4 * j + 3]);
+          for (int j = 0; j < 4; ++j) {
+            const f16x8 A = as_f16x8(ad[4 * j], ad[4 * j + 1], ad[4 * j + 2], ad[4 * j + 3]);
 #pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
-            acc[w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[w][s], 0, 0, 0);
+            for (int w = 0; w < NW; ++w) {
+              const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
+              acc[0][w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[0][w][s], 0, 0, 0);
+            }
+          }
+        }
+        return;
+      }
+      uint32_t ad[MSUB][16];
+#pragma unroll
+      for (int s = 0; s < MSUB; ++s)
+        if (s < nsub) codes32_to_f16<ABITS>(cur.a[s], ad[s]);
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        uint32_t bd[NW][16];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[q][w], cur.w[q][w], bd[w]);
+#pragma unroll
+        for (int s = 0; s < MSUB; ++s) {
+          if (s >= nsub) break;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f16x8 A = as_f16x8(ad[s][4 * j], ad[s][4 * j + 1], ad[s][4 * j + 2], ad[s][4 * j + 3]);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+              const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
+              acc[q][w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[q][w][s], 0, 0, 0);
+            }
           }
         }
       }
@@ -169,22 +206,28 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     if (ksplit) {
       if (wave > 0) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
+        for (int q = 0; q < NG; ++q)
 #pragma unroll
-          for (int s = 0; s < MSUB; ++s) red[(((wave - 1) * NW + w) * MSUB + s) * 64 + lane] = acc[w][s];
+          for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int s = 0; s < MSUB; ++s)
+              red[((((wave - 1) * NG + q) * NW + w) * MSUB + s) * 64 + lane] = acc[q][w][s];
       }
       __syncthreads();
       if (wave == 0) {
         for (int v = 1; v < splitk; ++v)
 #pragma unroll
-          for (int w = 0; w < NW; ++w)
+          for (int q = 0; q < NG; ++q)
 #pragma unroll
-            for (int s = 0; s < MSUB; ++s) acc[w][s] += red[(((v - 1) * NW + w) * MSUB + s) * 64 + lane];
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+              for (int s = 0; s < MSUB; ++s)
+                acc[q][w][s] += red[((((v - 1) * NG + q) * NW + w) * MSUB + s) * 64 + lane];
       }
     }
 
     // epilogue: lane holds D[m = 4*(lane>>4) + i][n = lane & 15]
-    if ((wave == 0 || rowsplit) && nvalid) {
+    if (wave == 0 || rowsplit) {
 #pragma unroll
       for (int s = 0; s < MSUB; ++s) {
 #pragma unroll
@@ -194,11 +237,15 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
           const int64_t r = r0 + m;
           const int64_t tok = row_token ? (int64_t)row_token[r] : r;
           const float sc = scales[tok];
-          if constexpr (NW == 2) {
-            const float gv = acc[0][s][i] * sc, uv = acc[1][s][i] * sc;
-            reinterpret_cast<uint16_t*>(out)[r * ldo + n] = f32_to_bf16_rne(silu_mul(gv, uv));
-          } else {
-            reinterpret_cast<float*>(out)[r * ldo + n] = acc[0][s][i] * sc;
+#pragma unroll
+          for (int q = 0; q < NG; ++q) {
+            if (!nvalid[q]) continue;
+            if constexpr (NW == 2) {
+              const float gv = acc[q][0][s][i] * sc, uv = acc[q][1][s][i] * sc;
+              reinterpret_cast<uint16_t*>(out)[r * ldo + nrow[q]] = f32_to_bf16_rne(silu_mul(gv, uv));
+            } else {
+              reinterpret_cast<float*>(out)[r * ldo + nrow[q]] = acc[q][0][s][i] * sc;
+            }
           }
         }
       }
@@ -207,28 +254,35 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   }
 }
 
-template <int BITS, int ABITS, int NW, int MSUB>
+template <int BITS, int ABITS, int NW, int MSUB, int NG>
 static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
-  dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)E);
-  const size_t lds = (size_t)(splitk - 1) * NW * MSUB * 64 * sizeof(f32x4);
-  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB>), grid, dim3(64 * splitk), lds,
+  dim3 grid((unsigned)((a.N + 16 * NG - 1) / (16 * NG)), (unsigned)E);
+  const size_t lds = (size_t)(splitk - 1) * NG * NW * MSUB * 64 * sizeof(f32x4);
+  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG>), grid, dim3(64 * splitk), lds,
                      stream, a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows,
                      a.N, a.K, splitk, max_rows, a.out, a.ldo);
   return hipGetLastError();
 }
 
+// Row groups per wave: a single matrix with 2- or 3-bit tables (8 VGPRs per row)
+// takes two, which halves the activation conversions; the gate/up pair and 4-bit
+// tables (32 VGPRs per row) keep one, as more registers would cost occupancy.
+static int decode_groups(int bits, int n_w) { return (n_w == 1 && bits <= 3) ? 2 : 1; }
+
 template <int BITS, int ABITS>
 static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStream_t s) {
-  if (a.n_w == 2) return launch_t<BITS, ABITS, 2, 2>(a, max_rows, splitk, s);
-  return launch_t<BITS, ABITS, 1, 2>(a, max_rows, splitk, s);
+  if (a.n_w == 2) return launch_t<BITS, ABITS, 2, 2, 1>(a, max_rows, splitk, s);
+  if constexpr (BITS <= 3) return launch_t<BITS, ABITS, 1, 2, 2>(a, max_rows, splitk, s);
+  else return launch_t<BITS, ABITS, 1, 2, 1>(a, max_rows, splitk, s);
 }
 
 hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream) {
   // enough waves per grid to keep HBM busy: split K (small experts) or rows (large)
   const int E = a.offsets ? a.E : 1;
   const int64_t active = a.offsets ? (a.n_rows < E ? a.n_rows : E) : 1;
-  const int64_t tiles = (int64_t)((a.N + 15) / 16) * (active > 0 ? active : 1);
+  const int ng = decode_groups(a.bits, a.n_w);
+  const int64_t tiles = (int64_t)((a.N + 16 * ng - 1) / (16 * ng)) * (active > 0 ? active : 1);
   const int nchunks = (a.K + 127) / 128;
   int splitk = 1;
   while (splitk < 16 && tiles * splitk < 4096 && splitk * 2 <= nchunks) splitk *= 2;
