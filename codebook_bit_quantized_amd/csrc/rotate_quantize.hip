@@ -4,8 +4,11 @@
 // the model; Tables 1 and 9: activations are quantised to 4 or 8 bits (A4W4, A8W4).
 //
 // Each thread owns 32 consecutive channels of one token (four 16-byte loads).  A
-// token takes G lanes, G the power of two >= K/32 when K <= 2048 (then 64/G tokens
-// share a wave), else a whole workgroup of ceil(K/2048) waves.  The transform runs
+// token takes G lanes, G the power of two >= K/32 when K <= 1024 (then 64/G tokens
+// share a wave), else a whole workgroup of ceil(K/2048) waves.  Between 1024 and
+// 2048 channels with K/32 not a power of two, tokens of K/32 lanes are packed back to
+// back in 1024-lane workgroups (a token may straddle two waves; its absmax then
+// meets in LDS), which keeps all but K/32 - 1 lanes of a workgroup busy.  The transform runs
 // in fp64, which is exact for bf16 inputs whose nonzero exponents in a block spread
 // at most 45 - log2(b) binades: five butterfly stages inside the thread, then one
 // lane exchange per further stage (DPP for lane distances 1, 2 and 8, ds_swizzle for
@@ -53,13 +56,16 @@ __device__ __forceinline__ float xor_lane_f32(float v) {
   return __builtin_bit_cast(float, xor_lane<M>(__builtin_bit_cast(int, v)));
 }
 
-// one butterfly stage between lanes j and j ^ M (M lanes = 32 * M channels apart)
+// one butterfly stage between lanes j and j ^ M (M lanes = 32 * M channels apart):
+// the lower lane keeps p + v, the upper one p + (-v), the sign flipped by one xor on
+// the high word instead of a select between two sums
 template <int M>
 __device__ __forceinline__ void lane_stage(double* v, bool upper) {
+  const uint64_t smask = upper ? 0x8000000000000000ull : 0ull;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const double p = xor_lane_f64<M>(v[i]);
-    v[i] = upper ? (p - v[i]) : (v[i] + p);
+    v[i] = p + __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, v[i]) ^ smask);
   }
 }
 
@@ -81,8 +87,9 @@ __device__ __forceinline__ void exp_range(double x, int& emin, int& emax) {
 
 }  // namespace
 
-// G: lanes per token (a power of two <= 64, or a multiple of 64 = the workgroup).
-__global__ void __launch_bounds__(512)
+// G: lanes per token (a power of two <= 64, or a multiple of 64 = the workgroup), or
+// 0 for K/32 lanes per token packed back to back in the workgroup.
+__global__ void __launch_bounds__(1024)
 rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, int K, int logb,
                        int G, int act_bits, float c_b, const float* __restrict__ smooth,
                        const uint8_t* __restrict__ signs, uint8_t* __restrict__ codes,
@@ -90,13 +97,21 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
   extern __shared__ double xchg[];          // cross-wave butterflies: [8][blockDim]
   __shared__ float red_max[8];
   __shared__ int red_emin[8], red_emax[8];
+  __shared__ uint32_t s_amax[32];            // packed mode: per-token absmax (float bits)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int nthr = K >> 5;
   int64_t t;
   int j;                                     // thread index within the token
-  if (G <= 64) {
+  int lt = 0;                                // packed mode: token within the workgroup
+  const int tpb = G == 0 ? (int)blockDim.x / nthr : 0;
+  if (G == 0) {
+    lt = tid / nthr;
+    j = tid - lt * nthr;
+    t = (int64_t)blockIdx.x * tpb + lt;
+    if (tid < 32) s_amax[tid] = 0u;
+  } else if (G <= 64) {
     const int tpw = 64 / G;                  // tokens per wave
     t = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * tpw + lane / G;
     j = lane & (G - 1);
@@ -104,7 +119,7 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
     t = blockIdx.x;
     j = tid;
   }
-  const bool active = t < T && j < nthr;
+  const bool active = t < T && j < nthr && lt < (G == 0 ? tpb : 1);
   const int b = 1 << logb;
 
   double v[32];
@@ -222,6 +237,21 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
     u[i] = (float)v[i];                      // round to nearest even
     amax = fmaxf(amax, fabsf(u[i]));
   }
+  if (G == 0) {
+    // reduce inside each Hadamard block (its lanes never straddle a wave or a
+    // token), then one LDS max per block; absmax >= 0, so the bits order as floats
+    const int gth = b >> 5;
+    if (gth > 1) amax = fmaxf(amax, xor_lane_f32<1>(amax));
+    if (gth > 2) amax = fmaxf(amax, xor_lane_f32<2>(amax));
+    if (gth > 4) amax = fmaxf(amax, xor_lane_f32<4>(amax));
+    if (gth > 8) amax = fmaxf(amax, xor_lane_f32<8>(amax));
+    if (gth > 16) amax = fmaxf(amax, xor_lane_f32<16>(amax));
+    if (gth > 32) amax = fmaxf(amax, xor_lane_f32<32>(amax));
+    __syncthreads();
+    if (active && (gth <= 1 || (j & (gth - 1)) == 0)) atomicMax(&s_amax[lt], __builtin_bit_cast(uint32_t, amax));
+    __syncthreads();
+    amax = lt < tpb ? __builtin_bit_cast(float, s_amax[lt]) : 0.0f;
+  }
   if (G > 1) amax = fmaxf(amax, xor_lane_f32<1>(amax));
   if (G > 2) amax = fmaxf(amax, xor_lane_f32<2>(amax));
   if (G > 4) amax = fmaxf(amax, xor_lane_f32<4>(amax));
@@ -243,9 +273,8 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
   int q[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    float r = rintf((float)((double)u[i] * rs));
-    r = fminf(fmaxf(r, lo), Q);
-    q[i] = (int)r;
+    const float r = rintf((float)((double)u[i] * rs));
+    q[i] = (int)__builtin_amdgcn_fmed3f(r, lo, Q);
   }
   if (active) {
     if (act_bits == 4) {
@@ -286,7 +315,12 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
   int G, threads;
   int64_t blocks;
   size_t lds = 0;
-  if (nthr <= 64) {
+  if (nthr > 32 && nthr < 64) {
+    G = 0;                                   // packed: K/32 lanes per token
+    threads = 1024;
+    const int64_t per_block = threads / nthr;
+    blocks = (T + per_block - 1) / per_block;
+  } else if (nthr <= 64) {
     G = 1;
     while (G < nthr) G <<= 1;
     threads = 256;

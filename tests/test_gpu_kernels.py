@@ -54,6 +54,21 @@ def test_rotate_quantize_explicit_blocks_and_stride(had_block):
     assert np.array_equal(scales.cpu().numpy(), ref["scale"])
 
 
+@pytest.mark.parametrize("K,had_block,act_bits", [(1056, 0, 4), (1088, 0, 8), (1408, 0, 4), (1536, 0, 8),
+                                                   (1984, 0, 4), (1408, 8, 8), (1408, 32, 4)])
+def test_rotate_quantize_packed_tokens(K, had_block, act_bits):
+    # K/32 lanes per token, not a power of two: tokens packed back to back, some of
+    # them straddling two waves; 50 tokens fill two workgroups and part of a third
+    T = 50
+    xb = datagen.random_tokens(K + 3 * act_bits, T, K + 32)  # ldx = K + 32
+    xb[7] = 0                                                # an all-zero token
+    ref = oracle.rotate_quantize(np.ascontiguousarray(xb[:, :K]), had_block, act_bits)
+    x = bf16_dev(xb)[:, :K]
+    codes, scales = cbq.rotate_quantize(x, act_bits, had_block=had_block)
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+    assert np.array_equal(scales.cpu().numpy(), ref["scale"])
+
+
 def test_rotate_quantize_golden_tie_example():
     v = np.array([1.5, 1.625, 1.125, 0, 0.375, 0.25, 1.75, 0.375])
     x = datagen.f32_to_bf16_bits(np.tile(v / 32.0, 32)[None, :].astype(np.float32))
