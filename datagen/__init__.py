@@ -44,6 +44,7 @@ TAG_UP_CB = 13
 TAG_DOWN_IDX = 14
 TAG_DOWN_CB = 15
 TAG_W_FULL = 16        # full-precision weights (input of codebook construction)
+TAG_ROT = 17           # dense rotation matrices
 TAG_MISC = 99
 
 OUTLIER_CHANNELS = (3, 77)
@@ -262,6 +263,21 @@ def dense_tokens(w: Workload, T: int, which: str = "gate_up") -> np.ndarray:
 # small random shapes for property tests (same distributions, any sizes)
 def random_weights(seed: int, E: int, N: int, K: int, bits: int, keep_raw: bool = True) -> WeightSet:
     return weight_set(1000 + seed, TAG_GATE_IDX, TAG_GATE_CB, E, N, K, bits, keep_raw)
+
+
+def rotation_bf16(seed: int, K: int, flush_binades: int = 7) -> np.ndarray:
+    """A seeded stand-in for a learned K x K rotation, as bf16 bits [K][K].
+
+    The matrix is Haar-random orthogonal (QR of a Gaussian matrix, column signs fixed
+    by the diagonal of R); entries smaller than 2^-flush_binades of the largest are set
+    to zero, so every row's nonzero exponents span at most flush_binades binades; then
+    each entry is rounded once to bf16."""
+    g = rng_for(seed, TAG_ROT).standard_normal((K, K))
+    q, r = np.linalg.qr(g)
+    q = q * np.sign(np.diag(r))[None, :]
+    m = np.abs(q).max()
+    q = np.where(np.abs(q) < m * 2.0 ** -flush_binades, 0.0, q)
+    return f32_to_bf16_bits(q.astype(np.float32))
 
 
 def random_tokens(seed: int, T: int, K: int) -> np.ndarray:

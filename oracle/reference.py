@@ -54,6 +54,7 @@ __all__ = [
     "lut_gemm_buckets", "route", "silu_mul_bf16", "round_f64_to_bf16_bits", "combine",
     "moe_layer", "ACT_LEVELS", "bf16_order_keys", "round_f64_to_f16_bits",
     "kmeans_precondition", "kmeans_row", "kmeans_codebooks",
+    "dense_rotation_precondition", "rotate_dense", "rotate_quantize_dense",
 ]
 
 # quantiser parameters per activation width: (Q, lower clamp, upper clamp)
@@ -258,6 +259,86 @@ def rotate_quantize(x_bits: np.ndarray, had_block: int, act_bits: int,
         u32, ok = rotate_values(v, b, sig)
     q, scale = quantize(u32, b, act_bits)
     return dict(codes=pack_codes(q, act_bits), q=q, scale=scale, u32=u32, b=b, ok=ok)
+
+
+# ---------------------------------------------------------------------------
+# dense rotation (CodeQuant2 Figure 1: a rotation fused into the model smooths the
+# activation outliers; CodeQuant abstract: the rotation may be learned).  A dense
+# orthogonal K x K matrix R in bf16 stands for a learned rotation: u = R x per token.
+def _exponents(a: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """floor(log2|a|) and the nonzero mask."""
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    _, ex = np.frexp(a)
+    return ex.astype(np.int64) - 1, a > 0
+
+
+def dense_rotation_precondition(x_bits: np.ndarray, R_bits: np.ndarray) -> np.ndarray:
+    """True for tokens whose u = R x is summed exactly by fp64 in any order.
+
+    bf16 x with exponent e is a multiple of 2^(e-7), so every product x_k R[j][k] is a
+    multiple of 2^(emin_x + emin_Rj - 14) and below 2^(emax_x + emax_Rj + 2) in size;
+    the K-term partial sums stay below 2^53 units when
+    (emax_x - emin_x) + (emax_Rj - emin_Rj) <= 37 - ceil(log2 K).  The check takes the
+    largest row spread of R (over rows with a nonzero entry) for every j."""
+    x = bf16_bits_to_f64(x_bits)
+    R = bf16_bits_to_f64(R_bits)
+    K = x.shape[1]
+    bound = 37 - int(math.ceil(math.log2(K)))
+    big = np.int64(1 << 40)
+    ex, nzx = _exponents(x)
+    dx = np.where(nzx, ex, -big).max(axis=1) - np.where(nzx, ex, big).min(axis=1)
+    er, nzr = _exponents(R)
+    rows = nzr.any(axis=1)
+    if not rows.any():
+        return np.ones(x.shape[0], dtype=bool)
+    dr = (np.where(nzr, er, -big).max(axis=1) - np.where(nzr, er, big).min(axis=1))[rows].max()
+    return (dx + dr <= bound) | ~nzx.any(axis=1)
+
+
+def _exact_dense_token(x: np.ndarray, R: np.ndarray) -> np.ndarray:
+    """R @ x for one token in exact integer arithmetic, each output rounded once to fp32."""
+    K = x.shape[0]
+    out = np.zeros(K, dtype=np.float32)
+    xs = [float(v) for v in x]
+    nzx = [v for v in xs if v != 0.0]
+    nzr = R[R != 0]
+    if not nzx or nzr.size == 0:
+        return out
+    sx = min(math.frexp(abs(v))[1] - 1 for v in nzx) - 7
+    sr = int(min(math.frexp(abs(float(v)))[1] - 1 for v in nzr)) - 7
+    nx = [int(math.ldexp(v, -sx)) for v in xs]
+    for j in range(K):
+        acc = 0
+        for k, r in enumerate(R[j]):
+            if r != 0.0 and nx[k]:
+                acc += nx[k] * int(math.ldexp(float(r), -sr))
+        out[j] = round_int_pow2_to_f32(acc, sx + sr)
+    return out
+
+
+def rotate_dense(x_bits: np.ndarray, R_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """u32 = fp32(exact R @ x) per token ([T][K] bf16 bits, R [K][K] bf16 bits).
+
+    Returns (u32 [T][K] float32, ok [T] bool).  Tokens inside the precondition are
+    summed in fp64 (exact, so any order gives the same value); the others in exact
+    integer arithmetic."""
+    x = bf16_bits_to_f64(x_bits)
+    R = bf16_bits_to_f64(R_bits)
+    ok = dense_rotation_precondition(x_bits, R_bits)
+    u32 = (x @ R.T).astype(np.float32)
+    for t in np.nonzero(~ok)[0]:
+        u32[t] = _exact_dense_token(x[t], R)
+    return u32, ok
+
+
+def rotate_quantize_dense(x_bits: np.ndarray, R_bits: np.ndarray, act_bits: int):
+    """Dense rotation, then the same quantiser with the factor 1 in the scale (R is
+    orthonormal, so no 1/sqrt(b) normalisation is left to apply).
+
+    Returns dict(codes=packed uint8, q=int8 [T][K], scale=float32 [T], u32, ok)."""
+    u32, ok = rotate_dense(x_bits, R_bits)
+    q, scale = quantize(u32, 1, act_bits)
+    return dict(codes=pack_codes(q, act_bits), q=q, scale=scale, u32=u32, ok=ok)
 
 
 # ---------------------------------------------------------------------------
