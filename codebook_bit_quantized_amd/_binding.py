@@ -23,7 +23,8 @@ PATH_AUTO, PATH_LUT, PATH_MFMA = 0, 1, 2
 AUTO_MAX_LUT_ROWS = 32
 
 # every symbol include/cbq.h declares
-EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_route_workspace", "cbq_moe_route_gather",
+EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_rotate_dense_workspace",
+            "cbq_rotate_quantize_dense", "cbq_route_workspace", "cbq_moe_route_gather",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
             "cbq_kmeans_codebooks", "cbq_cpu_lut_gemm", "cbq_status_string", "cbq_last_error",
             "cbq_version")
@@ -58,6 +59,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cbq_rotate_quantize": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
         "cbq_rotate_quantize_ex": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp, vp,
                                                   vp]),
+        "cbq_rotate_dense_workspace": (sz, [i64, i32]),
+        "cbq_rotate_quantize_dense": (ctypes.c_int, [vp, i64, i32, i64, vp, i32, vp, vp, vp, vp, sz,
+                                                     vp]),
         "cbq_route_workspace": (sz, [i64, i32, i32, i32]),
         "cbq_moe_route_gather": (ctypes.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                 vp, sz, vp]),
@@ -148,6 +152,37 @@ def rotate_quantize(x: torch.Tensor, act_bits: int = 4, had_block: int = 0,
         _check(lib.cbq_rotate_quantize_ex(_ptr(x), T, K, ldx, had_block, act_bits, _ptr(smooth),
                                           _ptr(signs), _ptr(codes), _ptr(scales), _ptr(precond),
                                           _stream(stream)))
+    return codes, scales
+
+
+def rotate_dense_workspace(T: int, K: int) -> int:
+    """Bytes of device workspace rotate_quantize_dense needs (cbq_rotate_dense_workspace)."""
+    return int(load_library().cbq_rotate_dense_workspace(T, K))
+
+
+def rotate_quantize_dense(x: torch.Tensor, R: torch.Tensor, act_bits: int = 4,
+                          codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                          precond: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          stream=None):
+    """x: bf16 [T][K], R: bf16 [K][K] (u = R x per token) on the GPU -> (codes, scales).
+
+    ws: optional uint8 device workspace of rotate_dense_workspace(T, K) bytes."""
+    lib = load_library()
+    _require_gpu(x, R, ws)
+    T, K = x.shape
+    if (T > 0 and x.stride(1) != 1) or not R.is_contiguous() or tuple(R.shape) != (K, K):
+        raise ValueError("x needs unit channel stride and R must be a contiguous [K][K] tensor")
+    if codes is None:
+        codes = torch.empty((T, K * act_bits // 8), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+    need = int(lib.cbq_rotate_dense_workspace(T, K))
+    if ws is None and T > 0:
+        ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.cbq_rotate_quantize_dense(_ptr(x), T, K, max(x.stride(0), K), _ptr(R), act_bits, _ptr(codes),
+                                         _ptr(scales), _ptr(precond), _ptr(ws), nbytes,
+                                         _stream(stream)))
     return codes, scales
 
 

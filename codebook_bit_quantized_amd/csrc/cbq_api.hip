@@ -88,6 +88,36 @@ CBQ_EXPORT int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int6
                                 scales, precond_violations, stream);
 }
 
+CBQ_EXPORT size_t cbq_rotate_dense_workspace(int64_t T, int32_t K) {
+  if (T < 0 || T > 0x7FFFFFFF || K < 64 || K % 64 || K > 16384) return 0;
+  return cbq::dense_rotation_workspace_bytes(T, K);
+}
+
+CBQ_EXPORT int cbq_rotate_quantize_dense(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
+                                         const uint16_t* R, int32_t act_bits, uint8_t* codes,
+                                         float* scales, uint32_t* precond_violations, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
+  if (T > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "T must be < 2^31");
+  if (K < 64 || K % 64) return fail(CBQ_EINVAL, "K must be a positive multiple of 64 (got %d)", K);
+  if (K > 16384) return fail(CBQ_EUNSUPPORTED, "K must be <= 16384 (got %d)", K);
+  if (ldx < K || ldx % 8) return fail(CBQ_EINVAL, "ldx must be >= K and a multiple of 8 (got %lld)", (long long)ldx);
+  if (act_bits != 4 && act_bits != 8) return fail(CBQ_EINVAL, "act_bits must be 4 or 8 (got %d)", act_bits);
+  if (T == 0) return CBQ_OK;
+  if (!x || !R || !codes || !scales) return fail(CBQ_EINVAL, "x, R, codes and scales must be non-null");
+  if (!aligned16(x) || !aligned16(R)) return fail(CBQ_EINVAL, "x and R must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(CBQ_EINVAL, "codes must be 8-byte aligned");
+  const size_t need = cbq::dense_rotation_workspace_bytes(T, K);
+  if (!ws || ws_bytes < need)
+    return fail(CBQ_EWORKSPACE, "dense rotation workspace of %zu bytes required (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(CBQ_EINVAL, "ws must be 16-byte aligned");
+  hipError_t e = cbq::launch_rotate_dense(x, T, K, ldx, R, act_bits, codes, scales,
+                                          precond_violations, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rotate_quantize_dense launch");
+  return CBQ_OK;
+}
+
 CBQ_EXPORT size_t cbq_route_workspace(int64_t T, int32_t E, int32_t topk, int32_t n_shared) {
   (void)topk; (void)n_shared;
   if (T <= 0 || E < 1 || E > 256 || T > (1 << 24)) return 0;

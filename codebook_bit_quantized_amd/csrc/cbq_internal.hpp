@@ -50,6 +50,11 @@ hipError_t launch_kmeans(const uint16_t* w, int64_t R, int K, int64_t ldw, int b
                          uint8_t* idx, uint16_t* codebook, int32_t* iters_done,
                          hipStream_t stream);
 
+size_t dense_rotation_workspace_bytes(int64_t T, int K);
+hipError_t launch_rotate_dense(const uint16_t* x, int64_t T, int K, int64_t ldx, const uint16_t* R,
+                               int act_bits, uint8_t* codes, float* scales, uint32_t* precond,
+                               void* ws, hipStream_t stream);
+
 hipError_t launch_combine(const float* expert_out, const int32_t* slot_of, const float* w,
                           int64_t T, int topk, int H, int n_shared, float* y, hipStream_t stream);
 

@@ -126,6 +126,33 @@ int cbq_rotate_quantize_ex(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
                            void* stream);
 
 /*
+ * cbq_rotate_quantize_dense - a dense K x K rotation before the quantiser.  Passage:
+ * CodeQuant2, Figure 1 (a rotation fused into the model smooths activation outliers);
+ * CodeQuant abstract (the rotation may be learned).  R stands for such a learned
+ * rotation (orthonormal, so the scale carries no normalisation factor).
+ *
+ *  x          : bf16 [T][ldx] (ldx >= K, ldx % 8 == 0, 16-byte aligned).
+ *  R          : bf16 [K][K] (16-byte aligned): u[j] = sum_k R[j][k] * x[k].
+ *  act_bits   : 4 or 8, codes and scales as in cbq_rotate_quantize (8-byte aligned codes).
+ *  precond_violations : optional device uint32 counter; incremented once per token
+ *               whose nonzero exponents spread more than 37 - ceil(log2 K) binades
+ *               minus the widest spread of a row of R, the bound under which the fp64
+ *               sums below are exact in any order.
+ *  ws, ws_bytes : device workspace of at least cbq_rotate_dense_workspace(T, K) bytes,
+ *               16-byte aligned; it holds fp32(u) between the two passes.
+ *
+ *  Computes u = R x exactly (bf16 products are exact in fp64; inside the bound so are
+ *  the sums), then v = fp32(u); M = max|v|; s = M / Q; q = clamp(rint_even(v / s));
+ *  scale = s.  A token with M == 0 gets codes 0 and scale 0.
+ *  Requires K % 64 == 0, 64 <= K <= 16384, T < 2^31.
+ */
+size_t cbq_rotate_dense_workspace(int64_t T, int32_t K);
+int cbq_rotate_quantize_dense(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
+                              const uint16_t* R, int32_t act_bits, uint8_t* codes, float* scales,
+                              uint32_t* precond_violations, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
  * cbq_moe_route_gather - top-k routing and per-expert row lists.
  * Passage: the AI Radio episode on CodeQuant (introduction: a router sends each input
  * to the right expert of the mixture).

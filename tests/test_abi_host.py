@@ -74,6 +74,23 @@ def test_rotate_quantize_ex_validation():
     assert ex(P, 0, 256, 256, 0, 4, P, P, P, P, None, None) == cbq.CBQ_OK          # empty
 
 
+def test_rotate_quantize_dense_validation():
+    lib = _lib()
+    P, U = _Fake.P, _Fake.UNALIGNED
+    rd = lib.cbq_rotate_quantize_dense
+    assert lib.cbq_rotate_dense_workspace(4, 256) == 4 * 256 * 4 + 256
+    assert lib.cbq_rotate_dense_workspace(4, 96) == 0                               # K % 64
+    need = lib.cbq_rotate_dense_workspace(4, 256)
+    assert rd(P, 4, 96, 96, P, 4, P, P, None, P, need, None) == cbq.CBQ_EINVAL      # K % 64
+    assert rd(P, 4, 256, 250, P, 4, P, P, None, P, need, None) == cbq.CBQ_EINVAL    # ldx
+    assert rd(P, 4, 256, 256, P, 5, P, P, None, P, need, None) == cbq.CBQ_EINVAL    # act_bits
+    assert rd(P, 4, 256, 256, U, 4, P, P, None, P, need, None) == cbq.CBQ_EINVAL    # R alignment
+    assert rd(P, 4, 256, 256, P, 4, P, P, None, P, need - 1, None) == cbq.CBQ_EWORKSPACE
+    assert rd(P, 4, 256, 256, P, 4, P, P, None, None, 0, None) == cbq.CBQ_EWORKSPACE
+    assert rd(P, 4, 32768, 32768, P, 4, P, P, None, P, need, None) == cbq.CBQ_EUNSUPPORTED
+    assert rd(None, 0, 256, 256, None, 4, None, None, None, None, 0, None) == cbq.CBQ_OK  # T = 0
+
+
 def test_route_validation():
     lib = _lib()
     P = _Fake.P
