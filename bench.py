@@ -41,6 +41,7 @@ import datagen  # noqa: E402
 METRIC = "MoE LUT-GEMM tokens/s + % HBM roofline (decode) / % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0
+F64_MFMA_PEAK_TFLOPS = 78.6
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "mfma_prefill": ["codebook_bit_quantized_amd/csrc/lut_gemm_prefill.hip",
@@ -500,6 +501,56 @@ def bench_kmeans(args, cbq, torch):
     print(json.dumps(line))
 
 
+def bench_dense_rotation(args, cbq, torch):
+    """The dense-rotation variant of rotate_quantize on the workload's layer input
+    (T prefill tokens x H channels, R a seeded H x H stand-in for a learned rotation):
+    tokens/s, and the fp64 matrix-core rate of the whole call against the fp64 MFMA peak
+    (the quantise pass is a few percent of it)."""
+    import oracle
+    wl = datagen.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    T, K = wl.T_list[0], wl.H
+    xb = datagen.activations_bf16(wl.wid, datagen.TAG_X, T, K)
+    Rb = datagen.rotation_bf16(wl.wid, K)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    R = torch.from_numpy(Rb.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = torch.empty((cbq.rotate_dense_workspace(T, K),), dtype=torch.uint8, device=dev)
+    codes, scales = cbq.rotate_quantize_dense(x, R, wl.act_bits, ws=ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(3, args.steps)):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        cbq.rotate_quantize_dense(x, R, wl.act_bits, codes=codes, scales=scales, ws=ws)
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) / 1000.0)
+    t = float(np.mean(times))
+    flops = 2.0 * T * K * K
+    tf = flops / t / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = 128
+        t0 = time.perf_counter()
+        oracle.rotate_quantize_dense(xb[:n], Rb, wl.act_bits)
+        dt = time.perf_counter() - t0
+        cpu = dict(value=n / dt, unit="tokens/s", cores=len(os.sched_getaffinity(0)), kind="oracle",
+                   sample=f"oracle dense rotation + quantisation of the first {n} tokens "
+                          f"({dt:.1f} s; numpy fp64, exact-integer fallback outside the bound)")
+    line = dict(metric="dense-rotation rotate_quantize tokens/s", value=round(T / t, 1),
+                unit="tokens/s", n_gpus=1, steps=len(times), warmup=1,
+                ms_per_step=round(t * 1000.0, 3), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="f64", data="synthetic",
+                config=dict(workload=f"dense_rotation_{wl.name}", tokens=T, K=K,
+                            act_bits=wl.act_bits),
+                roofline=dict(bound="mfma", achieved=round(tf, 2), peak=F64_MFMA_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(tf / F64_MFMA_PEAK_TFLOPS, 4), traffic=None,
+                              kernel="dense_rot_gemm + dense_quant (whole call)",
+                              avg_launch_us=round(t * 1e6, 1), algorithmic_flops=flops),
+                cpu_baseline=cpu, host=platform.node())
+    print(json.dumps(line))
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -518,6 +569,8 @@ def main():
                     help="measure GEMM latency per codebook width and run the cluster allocation")
     ap.add_argument("--kmeans", action="store_true",
                     help="measure offline codebook construction (per-row K-means) instead")
+    ap.add_argument("--dense-rotation", action="store_true",
+                    help="measure the dense K x K rotation variant of rotate_quantize instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -555,6 +608,9 @@ def main():
         return
     if args.latency_table:
         bench_latency_table(args, cbq, torch)
+        return
+    if args.dense_rotation:
+        bench_dense_rotation(args, cbq, torch)
         return
 
     wl = datagen.WORKLOADS[args.workload]
