@@ -192,6 +192,36 @@ def test_grouped_swiglu_and_down(path, bits, act_bits, T, E, k, S):
     assert_normwise(out.cpu().numpy(), ref, 1e-3, "down")
 
 
+@pytest.mark.parametrize("bits,act_bits,n_w", [(3, 4, 2), (4, 8, 2), (2, 4, 1), (3, 8, 1), (4, 4, 1)])
+@pytest.mark.parametrize("path", [cbq.PATH_AUTO, cbq.PATH_LUT])
+def test_many_tile_decode_gemm(bits, act_bits, n_w, path):
+    # 64 experts x 2080 rows: enough 16-row tiles that no wave splits K (the decode
+    # layout of the large MoE layers); K = 160 leaves a 32-channel chunk tail, N = 2080
+    # leaves part of the last two-group wave empty, and the row counts include
+    # empty experts, full 32-row blocks and one expert of 40 rows (two row blocks when
+    # forced onto the LUT path; AUTO sends it to the MFMA path)
+    E, N, K, T = 64, 2080, 160, 50
+    rng = np.random.default_rng(bits * 10 + act_bits + n_w)
+    counts = rng.integers(0, 6, E)
+    counts[[3, 17, 40]] = 0
+    counts[5], counts[9], counts[63] = 32, 16, 40
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    row_token = rng.integers(0, T, R).astype(np.int32)
+    xb = datagen.random_tokens(300 + bits, T, K)
+    rq = oracle.rotate_quantize(xb, 0, act_bits)
+    ws = [datagen.random_weights(40 + bits + m, E, N, K, bits, keep_raw=False) for m in range(n_w)]
+    Wd = [upload_weights(w) for w in ws]
+    out = cbq.codebook_lut_gemm(to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits, Wd,
+                                expert_offsets=to_dev(offsets), row_token=to_dev(row_token), path=path)
+    ref = [oracle.expert_gemm(rq["q"], rq["scale"], row_token, offsets, w.idx, w.codebook, K, bits)
+           for w in ws]
+    if n_w == 2:
+        assert_bf16_close(bf16_to_bits(out), oracle.silu_mul_bf16(ref[0], ref[1]), "swiglu")
+    else:
+        assert_normwise(out.cpu().numpy(), ref[0], 1e-3, "f32")
+
+
 def test_gemm_deterministic():
     wl, gate, up, down, x, lg = _moe_case(7, 200, 8, 2, 1, 256, 192, 4, 4)
     rq = oracle.rotate_quantize(x, 0, 4)
