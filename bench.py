@@ -569,6 +569,8 @@ def main():
                     help="measure GEMM latency per codebook width and run the cluster allocation")
     ap.add_argument("--kmeans", action="store_true",
                     help="measure offline codebook construction (per-row K-means) instead")
+    ap.add_argument("--path", choices=("choose", "lut", "mfma"), default="choose",
+                    help="GEMM path of every MoE phase: as AUTO would choose (default), or forced")
     ap.add_argument("--dense-rotation", action="store_true",
                     help="measure the dense K x K rotation variant of rotate_quantize instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -635,7 +637,8 @@ def main():
             offs = ph.rt["offsets"].cpu().numpy().astype(np.int64)
             counts = np.diff(offs)
             ph.counts = counts
-            ph.path_gu = ph.path_dn = choose_path(cbq, counts, wl.E)
+            ph.path_gu = ph.path_dn = (choose_path(cbq, counts, wl.E) if args.path == "choose" else
+                                       cbq.PATH_LUT if args.path == "lut" else cbq.PATH_MFMA)
             ph.decode = decode or T <= 64
             phases.append(ph)
     else:
