@@ -9,10 +9,12 @@
 // fp16 MFMA whose A operand holds up to 16 tokens' activation codes (exact in fp16),
 // so the integer x centroid products are exact and accumulate in fp32.
 //
-// Layout.  A workgroup owns 16 output rows n of one expert and `splitk` waves.  Lane l
-// serves row n0 + (l & 15) and channel slice (l >> 4) * 32 of each 128-channel chunk,
-// i.e. one 4*bits-byte load per chunk per matrix.  Rows of the expert are processed
-// in blocks of 32 (two 16-row MFMA sub-tiles sharing each dequantised weight).
+// Layout.  A workgroup owns NG groups of 16 output rows n of one expert (NG = 2 for a
+// single matrix with 2- or 3-bit tables, else 1) and `splitk` waves.  Lane l serves
+// row n0 + 16q + (l & 15) of group q and channel slice (l >> 4) * 32 of each
+// 128-channel chunk, i.e. one 4*bits-byte load per chunk per matrix and group.  Token
+// rows of the expert are processed in blocks of 32 (two 16-row MFMA sub-tiles sharing
+// each dequantised weight; the groups share each converted activation fragment).
 //  - An expert with at most 32 rows (decode) is split along K: wave w takes a range
 //    of chunks, and the partial sums are reduced through LDS in wave order
 //    (deterministic).  This multiplies the loads in flight per output row.
