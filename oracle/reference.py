@@ -55,6 +55,7 @@ __all__ = [
     "moe_layer", "ACT_LEVELS", "bf16_order_keys", "round_f64_to_f16_bits",
     "kmeans_precondition", "kmeans_row", "kmeans_codebooks",
     "dense_rotation_precondition", "rotate_dense", "rotate_quantize_dense",
+    "refit_row", "refit_codebooks", "output_error",
 ]
 
 # quantiser parameters per activation width: (Q, lower clamp, upper clamp)
@@ -631,3 +632,89 @@ def kmeans_codebooks(w_bits: np.ndarray, bits: int, max_iters: int):
     for r in range(R):
         idx[r], cb[r], it[r] = kmeans_row(w_bits[r], bits, max_iters)
     return idx, cb, it
+
+
+# ---------------------------------------------------------------------------
+# output-aware centroid refit (the AI Radio episode on CodeQuant: the centroids are
+# fine-tuned to minimise the error of the layer's output, not of the weights alone;
+# CodeQuant2, Figure 1 right: centroids and assignments are tuned after clustering)
+REFIT_PIVOT_REL = 1e-12
+
+
+def refit_row(w_bits: np.ndarray, a: np.ndarray, cb_bits: np.ndarray, x_bits: np.ndarray):
+    """New centroids for one row with its assignments a fixed.
+
+    Minimises sum_i (sum_k X[i][k] (w_k - c[a_k]))^2 over c, with X the bf16 calibration
+    activations [n][K]: with P[i][j] = sum_{k: a_k = j} X[i][k] and y = X w, the normal
+    equations (P^T P) c = P^T y over the non-empty clusters, solved by Cholesky in
+    cluster order.  A cluster whose pivot is at most 1e-12 of the largest diagonal
+    entry (it adds nothing independent to the output) is left out and the
+    factorisation restarts without it; a cluster left out keeps its old centroid and
+    its share P c moves to the right-hand side.  Empty clusters keep theirs too.  The sums P and y are exact (math.fsum); P^T P and P^T y are fp64 dot
+    products; the solution is rounded once to fp16.  Returns fp16 bits [L]."""
+    w = bf16_bits_to_f64(np.asarray(w_bits, dtype=np.uint16))
+    X = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    a = np.asarray(a, dtype=np.int64)
+    L = np.asarray(cb_bits).shape[0]
+    n = X.shape[0]
+    P = np.zeros((n, L))
+    for j in range(L):
+        m = a == j
+        if m.any():
+            for i in range(n):
+                P[i, j] = math.fsum(X[i, m])
+    y = np.array([math.fsum(X[i] * w) for i in range(n)])   # bf16 x bf16 products are exact
+    M = P.T @ P
+    b = P.T @ y
+    nonempty = [j for j in range(L) if (a == j).any()]
+    active = list(nonempty)
+    c = f16_bits_to_f64(np.asarray(cb_bits, dtype=np.uint16)).copy()
+    while active:
+        sub = M[np.ix_(active, active)]
+        thr = REFIT_PIVOT_REL * max(sub.diagonal().max(), 0.0)
+        Lc = np.zeros_like(sub)
+        bad = None
+        for p_ in range(len(active)):
+            d = sub[p_, p_] - float(np.dot(Lc[p_, :p_], Lc[p_, :p_]))
+            if not d > thr:
+                bad = p_
+                break
+            Lc[p_, p_] = math.sqrt(d)
+            for q in range(p_ + 1, len(active)):
+                Lc[q, p_] = (sub[q, p_] - float(np.dot(Lc[q, :p_], Lc[p_, :p_]))) / Lc[p_, p_]
+        if bad is not None:
+            del active[bad]
+            continue
+        # clusters left out keep their centroid: their share of the output moves to the
+        # right-hand side
+        fixed = [j for j in nonempty if j not in active]
+        rhs = P[:, active].T @ (y - P[:, fixed] @ c[fixed]) if fixed else b[active]
+        z = np.zeros(len(active))
+        for p_ in range(len(active)):
+            z[p_] = (rhs[p_] - float(np.dot(Lc[p_, :p_], z[:p_]))) / Lc[p_, p_]
+        sol = np.zeros(len(active))
+        for p_ in reversed(range(len(active))):
+            sol[p_] = (z[p_] - float(np.dot(Lc[p_ + 1:, p_], sol[p_ + 1:]))) / Lc[p_, p_]
+        c[active] = sol
+        break
+    out = np.asarray(cb_bits, dtype=np.uint16).copy()
+    new = round_f64_to_f16_bits(c)
+    keep = np.zeros(L, dtype=bool)
+    keep[active] = True
+    out[keep] = new[keep]
+    return out
+
+
+def refit_codebooks(w_bits: np.ndarray, idx: np.ndarray, cb_bits: np.ndarray, x_bits: np.ndarray):
+    """refit_row over every row (w_bits [R][K], idx [R][K] unpacked, cb_bits [R][L])."""
+    return np.stack([refit_row(w_bits[r], idx[r], cb_bits[r], x_bits) for r in range(w_bits.shape[0])])
+
+
+def output_error(w_bits: np.ndarray, idx: np.ndarray, cb_bits: np.ndarray, x_bits: np.ndarray) -> float:
+    """Relative output error ||X (W - W_hat)^T||_F / ||X W^T||_F of a clustered matrix."""
+    W = bf16_bits_to_f64(np.asarray(w_bits, dtype=np.uint16))
+    C = f16_bits_to_f64(np.asarray(cb_bits, dtype=np.uint16))
+    Wh = np.take_along_axis(C, np.asarray(idx, dtype=np.int64), axis=1)
+    X = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    return float(np.linalg.norm(X @ (W - Wh).T) / np.linalg.norm(X @ W.T))
+
