@@ -26,7 +26,7 @@ AUTO_MAX_LUT_ROWS = 32
 EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_rotate_dense_workspace",
             "cbq_rotate_quantize_dense", "cbq_route_workspace", "cbq_moe_route_gather",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
-            "cbq_kmeans_codebooks", "cbq_cpu_lut_gemm", "cbq_status_string", "cbq_last_error",
+            "cbq_kmeans_codebooks", "cbq_refit_codebooks", "cbq_cpu_lut_gemm", "cbq_status_string", "cbq_last_error",
             "cbq_version")
 
 
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                  i64, vp, sz, vp]),
         "cbq_moe_combine": (ctypes.c_int, [vp, vp, vp, i64, i32, i32, i32, vp, vp]),
         "cbq_kmeans_codebooks": (ctypes.c_int, [vp, i64, i32, i64, i32, i32, vp, vp, vp, vp]),
+        "cbq_refit_codebooks": (ctypes.c_int, [vp, i64, i32, i64, i32, vp, vp, i32, i64, vp, vp]),
         "cbq_cpu_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, W, vp, i64, i32, i32]),
         "cbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "cbq_last_error": (ctypes.c_char_p, []),
@@ -272,6 +273,22 @@ def kmeans_codebooks(w: torch.Tensor, bits: int, max_iters: int = 50, idx: Optio
     _check(lib.cbq_kmeans_codebooks(_ptr(w), R, K, w.stride(0), bits, max_iters, _ptr(idx),
                                     _ptr(codebook), _ptr(iters_done), _stream(stream)))
     return CodebookWeights(idx=idx, codebook=codebook, K=K, bits=bits)
+
+
+def refit_codebooks(w: torch.Tensor, cw: "CodebookWeights", x: torch.Tensor, stream=None) -> "CodebookWeights":
+    """Output-aware refit of cw's centroids (in place) on bf16 calibration activations
+    x [n][K] (cbq_refit_codebooks); w: the bf16 rows [R][K] that cw clusters."""
+    lib = load_library()
+    _require_gpu(w, x, cw.idx, cw.codebook)
+    R, K = w.shape
+    n = x.shape[0]
+    if w.stride(1) != 1 or x.stride(1) != 1 or x.shape[1] != K or K != cw.K:
+        raise ValueError("w and x need contiguous rows of the weights' K channels")
+    if not cw.codebook.is_contiguous() or not cw.idx.is_contiguous():
+        raise ValueError("the codebook and index tensors must be contiguous")
+    _check(lib.cbq_refit_codebooks(_ptr(w), R, K, w.stride(0), cw.bits, _ptr(cw.idx), _ptr(x), n,
+                                   x.stride(0), _ptr(cw.codebook), _stream(stream)))
+    return cw
 
 
 CPU_NO_AVX512 = 1

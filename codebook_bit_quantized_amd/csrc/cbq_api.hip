@@ -241,6 +241,27 @@ CBQ_EXPORT int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int
   return CBQ_OK;
 }
 
+CBQ_EXPORT int cbq_refit_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw, int32_t bits,
+                                   const uint8_t* idx, const uint16_t* x, int32_t n, int64_t ldx,
+                                   uint16_t* codebook, void* stream) {
+  g_err[0] = 0;
+  if (R < 0) return fail(CBQ_EINVAL, "R must be >= 0 (got %lld)", (long long)R);
+  if (R > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "R must be < 2^31");
+  if (K < 32 || K % 32) return fail(CBQ_EINVAL, "K must be a positive multiple of 32 (got %d)", K);
+  if (K > 16384) return fail(CBQ_EUNSUPPORTED, "K must be <= 16384 (got %d)", K);
+  if (ldw < K || ldx < K) return fail(CBQ_EINVAL, "ldw and ldx must be >= K");
+  if (bits < 2 || bits > 4) return fail(CBQ_EUNSUPPORTED, "bits must be 2, 3 or 4 (got %d)", bits);
+  if (n < 1 || n > 256) return fail(CBQ_EINVAL, "n must be in [1, 256] (got %d)", n);
+  if (R == 0) return CBQ_OK;
+  if (!w || !idx || !x || !codebook) return fail(CBQ_EINVAL, "w, idx, x and codebook must be non-null");
+  if ((reinterpret_cast<uintptr_t>(w) & 1u) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+      (reinterpret_cast<uintptr_t>(codebook) & 1u))
+    return fail(CBQ_EINVAL, "w, x and codebook must be 2-byte aligned");
+  hipError_t e = cbq::launch_refit(w, R, K, ldw, bits, idx, x, n, ldx, codebook, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "refit_codebooks launch");
+  return CBQ_OK;
+}
+
 CBQ_EXPORT int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits,
                                 int64_t T, const cbq_weights* W, float* out, int64_t ldo,
                                 int32_t n_threads, int32_t flags) {

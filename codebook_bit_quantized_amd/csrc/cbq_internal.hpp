@@ -50,6 +50,9 @@ hipError_t launch_kmeans(const uint16_t* w, int64_t R, int K, int64_t ldw, int b
                          uint8_t* idx, uint16_t* codebook, int32_t* iters_done,
                          hipStream_t stream);
 
+hipError_t launch_refit(const uint16_t* w, int64_t R, int K, int64_t ldw, int bits, const uint8_t* idx,
+                        const uint16_t* x, int n, int64_t ldx, uint16_t* codebook, hipStream_t stream);
+
 size_t dense_rotation_workspace_bytes(int64_t T, int K);
 hipError_t launch_rotate_dense(const uint16_t* x, int64_t T, int K, int64_t ldx, const uint16_t* R,
                                int act_bits, uint8_t* codes, float* scales, uint32_t* precond,

@@ -300,6 +300,163 @@ static void launch_bits(int kpl, dim3 grid, size_t lds, hipStream_t stream, cons
   }
 }
 
+// Output-aware refit of a row's centroids with its assignments fixed (the AI Radio
+// episode on CodeQuant: centroids fine-tuned to minimise the layer's output error;
+// CodeQuant2, Figure 1 right: centroids tuned after clustering).  One wave per row:
+//  1. the row's assignments into LDS, and the mask of non-empty clusters;
+//  2. for each calibration row i: P[i][j] = sum over k in cluster j of X[i][k] and
+//     y[i] = sum_k X[i][k] w_k (lane partial sums, then a butterfly), into LDS;
+//  3. M = P^T P and b = P^T y, one entry per lane and pass;
+//  4. on lane 0: Cholesky over the non-empty clusters in index order; a pivot at most
+//     1e-12 of the largest diagonal entry drops that cluster (it keeps its centroid,
+//     its share P c moves to the right-hand side) and the factorisation restarts;
+//     then the two triangular solves and one rounding to fp16.
+template <int BITS>
+__global__ void __launch_bounds__(64)
+refit_rows_kernel(const uint16_t* __restrict__ w, int64_t ldw, int K, const uint8_t* __restrict__ idx,
+                  const uint16_t* __restrict__ x, int n, int64_t ldx, uint16_t* __restrict__ codebook) {
+  constexpr int L = 1 << BITS;
+  extern __shared__ __attribute__((aligned(16))) double rsm[];
+  double* sP = rsm;                  // [n][L]
+  double* sy = sP + n * L;           // [n]
+  double* sM = sy + n;               // [L][L]
+  double* sb = sM + L * L;           // [L]
+  double* sC = sb + L;               // [L][L] Cholesky factor
+  uint8_t* sa = reinterpret_cast<uint8_t*>(sC + L * L);   // [K]
+  const int lane = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int rb = K * BITS / 8;
+  const uint8_t* ir = idx + r * (int64_t)rb;
+  const uint16_t* wr = w + r * ldw;
+
+  uint32_t used = 0;
+  for (int k = lane; k < K; k += 64) {
+    const int bit = k * BITS, byte = bit >> 3;
+    const uint32_t v = ir[byte] | (byte + 1 < rb ? (uint32_t)ir[byte + 1] << 8 : 0u);
+    const uint32_t a = (v >> (bit & 7)) & (L - 1);
+    sa[k] = (uint8_t)a;
+    used |= 1u << a;
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) used |= (uint32_t)__shfl_xor((int)used, d);
+  __syncthreads();
+
+  for (int i = 0; i < n; ++i) {
+    double p[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) p[j] = 0.0;
+    double yy = 0.0;
+    const uint16_t* xi = x + (int64_t)i * ldx;
+    for (int k = lane; k < K; k += 64) {
+      const double xv = bf16_bits_to_f64(xi[k]);
+      const int a = sa[k];
+#pragma unroll
+      for (int j = 0; j < L; ++j) p[j] += a == j ? xv : 0.0;
+      yy = __builtin_fma(xv, bf16_bits_to_f64(wr[k]), yy);   // the product is exact
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+      for (int j = 0; j < L; ++j) p[j] += __shfl_xor(p[j], d);
+      yy += __shfl_xor(yy, d);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < L; ++j) sP[i * L + j] = p[j];
+      sy[i] = yy;
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < L * L + L; e += 64) {
+    double acc = 0.0;
+    if (e < L * L) {
+      const int j1 = e / L, j2 = e % L;
+      for (int i = 0; i < n; ++i) acc = __builtin_fma(sP[i * L + j1], sP[i * L + j2], acc);
+      sM[e] = acc;
+    } else {
+      const int j = e - L * L;
+      for (int i = 0; i < n; ++i) acc = __builtin_fma(sP[i * L + j], sy[i], acc);
+      sb[j] = acc;
+    }
+  }
+  __syncthreads();
+  if (lane != 0) return;
+
+  uint16_t* cr = codebook + r * L;
+  double c[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) c[j] = (double)__builtin_bit_cast(_Float16, cr[j]);
+  uint32_t act = used;
+  for (;;) {
+    if (act == 0) return;
+    int ix[L], na = 0;
+    for (int j = 0; j < L; ++j)
+      if (act >> j & 1u) ix[na++] = j;
+    double dmax = 0.0;
+    for (int q = 0; q < na; ++q) dmax = fmax(dmax, sM[ix[q] * L + ix[q]]);
+    const double thr = 1e-12 * dmax;
+    int bad = -1;
+    for (int p_ = 0; p_ < na && bad < 0; ++p_) {
+      double d = sM[ix[p_] * L + ix[p_]];
+      for (int t = 0; t < p_; ++t) d -= sC[p_ * L + t] * sC[p_ * L + t];
+      if (!(d > thr)) { bad = p_; break; }
+      const double lpp = sqrt(d);
+      sC[p_ * L + p_] = lpp;
+      for (int q = p_ + 1; q < na; ++q) {
+        double s = sM[ix[q] * L + ix[p_]];
+        for (int t = 0; t < p_; ++t) s -= sC[q * L + t] * sC[p_ * L + t];
+        sC[q * L + p_] = s / lpp;
+      }
+    }
+    if (bad >= 0) { act &= ~(1u << ix[bad]); continue; }
+    // right-hand side: clusters left out keep their centroid and their output share
+    double rhs[L];
+    const uint32_t fixed = used & ~act;
+    for (int q = 0; q < na; ++q) {
+      if (fixed == 0) { rhs[q] = sb[ix[q]]; continue; }
+      double s = 0.0;
+      for (int i = 0; i < n; ++i) {
+        double yi = sy[i];
+        for (int j = 0; j < L; ++j)
+          if (fixed >> j & 1u) yi -= sP[i * L + j] * c[j];
+        s += sP[i * L + ix[q]] * yi;
+      }
+      rhs[q] = s;
+    }
+    double z[L], sol[L];
+    for (int p_ = 0; p_ < na; ++p_) {
+      double s = rhs[p_];
+      for (int t = 0; t < p_; ++t) s -= sC[p_ * L + t] * z[t];
+      z[p_] = s / sC[p_ * L + p_];
+    }
+    for (int p_ = na - 1; p_ >= 0; --p_) {
+      double s = z[p_];
+      for (int t = p_ + 1; t < na; ++t) s -= sC[t * L + p_] * sol[t];
+      sol[p_] = s / sC[p_ * L + p_];
+    }
+    for (int q = 0; q < na; ++q) cr[ix[q]] = (uint16_t)f64_to_f16_rne(sol[q]);
+    return;
+  }
+}
+
+size_t refit_lds_bytes(int K, int bits, int n) {
+  const int L = 1 << bits;
+  return (size_t)(n * L + n + 2 * L * L + L) * sizeof(double) + (size_t)((K + 15) & ~15);
+}
+
+hipError_t launch_refit(const uint16_t* w, int64_t R, int K, int64_t ldw, int bits, const uint8_t* idx,
+                        const uint16_t* x, int n, int64_t ldx, uint16_t* codebook, hipStream_t stream) {
+  const size_t lds = refit_lds_bytes(K, bits, n);
+  const dim3 grid((unsigned)R);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(refit_rows_kernel<2>, grid, dim3(64), lds, stream, w, ldw, K, idx, x, n, ldx, codebook); break;
+    case 3: hipLaunchKernelGGL(refit_rows_kernel<3>, grid, dim3(64), lds, stream, w, ldw, K, idx, x, n, ldx, codebook); break;
+    case 4: hipLaunchKernelGGL(refit_rows_kernel<4>, grid, dim3(64), lds, stream, w, ldw, K, idx, x, n, ldx, codebook); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_kmeans(const uint16_t* w, int64_t R, int K, int64_t ldw, int bits, int max_iters,
                          uint8_t* idx, uint16_t* codebook, int32_t* iters_done,
                          hipStream_t stream) {

@@ -264,6 +264,30 @@ int cbq_kmeans_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw, i
                          int32_t* iters_done, void* stream);
 
 /*
+ * cbq_refit_codebooks - output-aware refit of clustered rows' centroids on calibration
+ * activations, assignments fixed.  Passage: the AI Radio episode on CodeQuant (the
+ * centroids are fine-tuned to minimise the error of the layer's output, looking at how
+ * the weights meet the activations); CodeQuant2, Figure 1 (right: centroids tuned after
+ * clustering).
+ *
+ *  w        : bf16 [R][ldw] original weight rows (ldw >= K).
+ *  idx      : [R][K*bits/8] the rows' assignments (LSB-first bitstream, as cbq_weights).
+ *  x        : bf16 [n][ldx] calibration activations (1 <= n <= 256, ldx >= K).
+ *  codebook : fp16 [R][2^bits], 2-byte aligned; read as the current centroids and
+ *             overwritten with the refit ones.
+ *
+ *  Per row, with P[i][j] = sum over k assigned to j of x[i][k] and y = x w: solve
+ *  (P^T P) c = P^T y over the non-empty clusters by Cholesky in index order; a cluster
+ *  whose pivot is at most 1e-12 of the largest diagonal entry keeps its centroid (its
+ *  share P c moves to the right-hand side) and the factorisation restarts without it;
+ *  empty clusters keep theirs.  The sums run in fp64; each new centroid is rounded once
+ *  to fp16.  Requires K % 32 == 0, 32 <= K <= 16384, bits in 2..4.
+ */
+int cbq_refit_codebooks(const uint16_t* w, int64_t R, int32_t K, int64_t ldw, int32_t bits,
+                        const uint8_t* idx, const uint16_t* x, int32_t n, int64_t ldx,
+                        uint16_t* codebook, void* stream);
+
+/*
  * cbq_cpu_lut_gemm - the same codebook-LUT GEMM on host cores (x86-64 with AVX2, FMA,
  * F16C and BMI2).  Passage: CodeQuant abstract (dedicated kernels for GPU and CPU) and the
  * AI Radio episode, "Improvements" (a CPU speedup from looking products up).

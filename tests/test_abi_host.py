@@ -91,6 +91,18 @@ def test_rotate_quantize_dense_validation():
     assert rd(None, 0, 256, 256, None, 4, None, None, None, None, 0, None) == cbq.CBQ_OK  # T = 0
 
 
+def test_refit_validation():
+    lib = _lib()
+    P = _Fake.P
+    rf = lib.cbq_refit_codebooks
+    assert rf(P, 4, 96, 96, 3, P, P, 0, 96, P, None) == cbq.CBQ_EINVAL        # n = 0
+    assert rf(P, 4, 96, 96, 3, P, P, 257, 96, P, None) == cbq.CBQ_EINVAL      # n > 256
+    assert rf(P, 4, 100, 100, 3, P, P, 8, 100, P, None) == cbq.CBQ_EINVAL     # K % 32
+    assert rf(P, 4, 96, 96, 5, P, P, 8, 96, P, None) == cbq.CBQ_EUNSUPPORTED  # bits
+    assert rf(P, 4, 96, 64, 3, P, P, 8, 96, P, None) == cbq.CBQ_EINVAL        # ldw < K
+    assert rf(None, 0, 96, 96, 3, None, None, 8, 96, None, None) == cbq.CBQ_OK  # R = 0
+
+
 def test_route_validation():
     lib = _lib()
     P = _Fake.P
