@@ -488,12 +488,39 @@ def bench_kmeans(args, cbq, torch):
         dt = time.perf_counter() - t0
         cpu = dict(value=n / dt, unit="rows/s", cores=1, kind="oracle",
                    sample=f"oracle per-row K-means on the first {n} rows ({dt:.1f} s, numpy fp64)")
+    # output-aware refit on 128 calibration tokens of the layer input; its effect on the
+    # output error is measured by the oracle on held-out tokens for a sample of rows
+    n_cal = 128
+    xc_np = datagen.activations_bf16(wl.wid, datagen.TAG_X_DECODE, n_cal, K)
+    xt_np = datagen.activations_bf16(wl.wid + 1, datagen.TAG_X_DECODE, n_cal, K)
+    xc = torch.from_numpy(xc_np.view(np.int16)).to(dev)
+    cb0 = cw.codebook.clone()
+    rtimes = []
+    for _ in range(max(1, args.steps // 4)):
+        cw.codebook.copy_(cb0)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        cbq.refit_codebooks(w, cw, xc)
+        e.record()
+        torch.cuda.synchronize()
+        rtimes.append(s.elapsed_time(e) / 1000.0)
+    tr = float(np.median(rtimes))
+    rows = np.arange(0, R, max(1, R // 256))[:256]
+    idx_np = oracle.unpack_indices(cw.idx.cpu().numpy().reshape(R, -1)[rows], K, bits)
+    cb_before = cb0.cpu().numpy().reshape(R, -1)[rows].view(np.uint16)
+    cb_after = cw.codebook.cpu().numpy().reshape(R, -1)[rows].view(np.uint16)
+    err0 = oracle.output_error(w_np[rows], idx_np, cb_before, xt_np)
+    err1 = oracle.output_error(w_np[rows], idx_np, cb_after, xt_np)
+    refit = dict(rows_per_s=round(R / tr, 1), ms=round(tr * 1000.0, 3), calibration_tokens=n_cal,
+                 held_out_output_error_kmeans=round(err0, 5), held_out_output_error_refit=round(err1, 5),
+                 sample_rows=int(len(rows)))
     line = dict(metric="codebook construction rows/s", value=round(R / t, 1), unit="rows/s",
                 n_gpus=1, steps=len(times), warmup=1, ms_per_step=round(t * 1000.0, 3),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f64",
                 data="synthetic",
                 config=dict(workload=f"kmeans_gate_{wl.name}", rows=R, K=K, bits=bits,
                             max_iters=max_iters, mean_rounds=round(float(rounds.mean()), 2)),
+                refit=refit,
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
                               kernel="kmeans_rows", algorithmic_bytes=nbytes),
