@@ -6,7 +6,8 @@
 // rows grouped expert by expert with tokens ascending; shared experts after.
 //
 // Kernel 1: one wave per token; the k winners are found by k rounds of a wave-wide
-// max over 64-bit keys (order-preserving logit bits, then inverted expert id).
+// max over 64-bit keys (order-preserving logit bits, then inverted expert id), with
+// DPP row rotations and scalar lane reads rather than LDS permutes.
 // Kernel 2: one workgroup does a counting sort by (expert, token).  Ranks come from
 // per-expert token bitmaps, never from the order of atomics, so every integer output
 // is deterministic.
@@ -24,10 +25,81 @@ __device__ __forceinline__ float from_order_bits(uint32_t o) {
   return __builtin_bit_cast(float, u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
+// value of the lane n places down the same row of 16 (DPP row rotate)
+template <int N>
+__device__ __forceinline__ uint64_t row_ror_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x120 + N, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), 0x120 + N, 0xF, 0xF, false);
   return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// maximum over the wave, in every lane: rotations by 1, 2, 4 and 8 inside each row of
+// 16 lanes (DPP, a few cycles each), then the four row maxima read as scalars
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o = row_ror_u64<1>(v); v = o > v ? o : v;
+  o = row_ror_u64<2>(v); v = o > v ? o : v;
+  o = row_ror_u64<4>(v); v = o > v ? o : v;
+  o = row_ror_u64<8>(v); v = o > v ? o : v;
+  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
+  const uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
+// The k winners of token t, ids sel_id[0..k) and their softmax weights, in every lane.
+// Called by whole waves only: the DPP rotations read every lane of a row.
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int64_t t, int E,
+                                           int topk, int renormalize, int lane, int* sel_id,
+                                           float* sel_w) {
+  const float* row = logits + t * E;
+  constexpr int PER = 4;   // E <= 256
+  uint64_t key[PER];
+  float val[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    val[i] = e < E ? row[e] : 0.0f;
+    key[i] = e < E ? (((uint64_t)order_bits(val[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+  }
+  float sel_v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= topk) break;
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    sel_id[j] = e;
+    sel_v[j] = from_order_bits((uint32_t)(best >> 32));
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i == e) key[i] = 0ull;
+  }
+  const float vmax = sel_v[0];
+  float denom;
+  if (renormalize) {
+    denom = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < topk) denom += expf(sel_v[j] - vmax);
+  } else {
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i < E) part += expf(val[i] - vmax);
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    denom = part;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < topk) sel_w[j] = expf(sel_v[j] - vmax) / denom;
 }
 
 // One wave per token; workgroup c (16 waves) takes the tokens of chunk c and also
@@ -44,56 +116,15 @@ route_topk_kernel(const float* __restrict__ logits, int64_t T, int E, int topk, 
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   const int64_t c1 = c0 + chunk < T ? c0 + chunk : T;
   for (int64_t t = c0 + wave; t < c1; t += 16) {
-    const float* row = logits + t * E;
-    constexpr int PER = 4;   // E <= 256
-    uint64_t key[PER];
-    float val[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      val[i] = e < E ? row[e] : 0.0f;
-      key[i] = e < E ? (((uint64_t)order_bits(val[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e)) : 0ull;
-    }
     int sel_id[8];
-    float sel_v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= topk) break;
-      uint64_t best = key[0];
-#pragma unroll
-      for (int i = 1; i < PER; ++i) best = key[i] > best ? key[i] : best;
-      for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = shfl_xor_u64(best, m);
-        best = o > best ? o : best;
-      }
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      sel_id[j] = e;
-      sel_v[j] = from_order_bits((uint32_t)(best >> 32));
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (lane + 64 * i == e) key[i] = 0ull;
-    }
-    const float vmax = sel_v[0];
-    float denom;
-    if (renormalize) {
-      denom = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < topk) denom += expf(sel_v[j] - vmax);
-    } else {
-      float part = 0.0f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (lane + 64 * i < E) part += expf(val[i] - vmax);
-      for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
-      denom = part;
-    }
+    float sel_w[8];
+    topk_token(logits, t, E, topk, renormalize, lane, sel_id, sel_w);
     if (lane == 0) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < topk) {
           ids[t * topk + j] = sel_id[j];
-          wts[t * topk + j] = expf(sel_v[j] - vmax) / denom;
+          wts[t * topk + j] = sel_w[j];
           atomicAdd(&s_cnt[sel_id[j]], 1);
         }
       }
