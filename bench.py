@@ -10,9 +10,11 @@ of the workload; for a dense workload it is rotate+quantise and the GEMM of each
 its two linears for every batch size.
 
 The default workload is the 64-routed + 2-shared expert layer (hidden 2048, FFN 1408,
-top-6, 3-bit gate/up and 2-bit down codebooks, A4): a 4096-token prefill followed by a
+top-6, 3-bit gate/up and 2-bit down codebooks, A4): a 4096-token prefill batch and a
 32-token decode batch, the one workload that exercises every step of the path
-including both GEMM inner paths.
+including both GEMM inner paths.  The decode batch runs on a second stream once the
+prefill gate/up GEMM is issued, and both finish inside the step
+(--decode-overlap serial runs them one after the other on one stream).
 
 Prints one JSON line: tokens/s over the timed steps; the roofline of the dominant
 kernel (the gate/up GEMM of the largest batch: against the fp16 MFMA peak when it
@@ -127,7 +129,7 @@ class MoEPhase:
         self.path_gu, self.path_dn = path_gu, path_dn
         self.ev = None   # (start, end) events around the gate/up GEMM when timing it
 
-    def run(self, stream=None):
+    def run(self, stream=None, after_gate_up=None):
         cbq, wl, W = self.cbq, self.wl, self.W
         a = wl.act_bits
         cbq.rotate_quantize(self.x, a, codes=self.codes, scales=self.scales, stream=stream)
@@ -140,6 +142,8 @@ class MoEPhase:
                               stream=stream)
         if self.ev is not None:
             self.ev[1].record()
+        if after_gate_up is not None:
+            after_gate_up()
         cbq.rotate_quantize(self.h, a, codes=self.codes_h, scales=self.scales_h, stream=stream)
         cbq.codebook_lut_gemm(self.codes_h, self.scales_h, a, [W["down"]], n_rows=self.R,
                               expert_offsets=self.rt["offsets"], path=self.path_dn, out=self.out,
@@ -600,6 +604,9 @@ def main():
                     help="GEMM path of every MoE phase: as AUTO would choose (default), or forced")
     ap.add_argument("--dense-rotation", action="store_true",
                     help="measure the dense K x K rotation variant of rotate_quantize instead")
+    ap.add_argument("--decode-overlap", choices=("down", "serial"), default="down",
+                    help="down: the decode batch runs on a second stream, beside the prefill "
+                         "batch's down projection; serial: after the prefill batch, on one stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -683,17 +690,40 @@ def main():
     dom = max(phases, key=lambda p: p.R)
     start_evs, end_evs = [], []
 
+    # A prefill batch and a decode batch are independent.  The decode batch runs on a
+    # second stream (default priority), released once the prefill gate/up GEMM has been
+    # issued, so its latency-bound kernels share the GPU with the prefill batch's
+    # rotate_quantize of h and down GEMM, not with the dominant kernel.  The two streams
+    # join at the end of every step, as one serving iteration would.
+    side = None
+    if (wl.kind == "moe" and len(phases) == 2 and phases[1].decode and not phases[0].decode
+            and args.decode_overlap != "serial"):
+        side = torch.cuda.Stream()
+
+    def run_step():
+        if side is None:
+            for ph in phases:
+                ph.run()
+            return
+        main_s = torch.cuda.current_stream()
+
+        def launch_decode():
+            side.wait_stream(main_s)
+            with torch.cuda.stream(side):
+                phases[1].run()
+
+        phases[0].run(after_gate_up=launch_decode)
+        main_s.wait_stream(side)
+
     for _ in range(args.warmup):
-        for ph in phases:
-            ph.run()
+        run_step()
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     for _ in range(args.steps):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         dom.ev = (s, e)
-        for ph in phases:
-            ph.run()
+        run_step()
         start_evs.append(s)
         end_evs.append(e)
     torch.cuda.synchronize()
@@ -769,7 +799,8 @@ def main():
         cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
                    hidden=wl.H, ffn=wl.F, experts=wl.E, shared_experts=wl.n_shared, topk=wl.topk,
                    bits_gate_up=wl.bits_gate_up, bits_down=wl.bits_down, act_bits=wl.act_bits,
-                   paths={str(p.T): int(p.path_gu) for p in phases})
+                   paths={str(p.T): int(p.path_gu) for p in phases},
+                   decode_overlap=args.decode_overlap if side is not None else "serial")
     else:
         cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
                    linears=[f"{wl.K}->{wl.N}", f"{wl.N}->{wl.K}"], bits=wl.bits,
