@@ -59,7 +59,10 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   extern __shared__ f32x4 red[];   // [(splitk-1) * NG * NW * MSUB][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e = blockIdx.y;
+  // Experts in reverse order: the shared experts come last in the row order and always
+  // hold every token, the most rows of any expert, so their longer waves start first
+  // instead of forming the tail of the grid.
+  const int e = gridDim.y - 1 - blockIdx.y;
   int64_t r0, me;
   if (offsets) {
     r0 = offsets[e];
