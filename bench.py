@@ -159,6 +159,26 @@ class MoEPhase:
                                    out=self.h)
 
 
+def run_mixed_step(torch, phases, side=None):
+    """One step over the phases.  Without `side`, one phase after the other on the
+    current stream.  With it (a prefill phase then a decode phase), the decode phase
+    runs on `side`, released once the prefill gate/up GEMM is issued, and the current
+    stream waits for it at the end."""
+    if side is None:
+        for ph in phases:
+            ph.run()
+        return
+    main_s = torch.cuda.current_stream()
+
+    def launch_decode():
+        side.wait_stream(main_s)
+        with torch.cuda.stream(side):
+            phases[1].run()
+
+    phases[0].run(after_gate_up=launch_decode)
+    main_s.wait_stream(side)
+
+
 class DensePhase:
     """Device buffers and the call sequence for the two decode linears of a dense
     workload over T tokens: rotate+quantise then GEMM, for 2560 -> 9728 and for
@@ -701,19 +721,7 @@ def main():
         side = torch.cuda.Stream()
 
     def run_step():
-        if side is None:
-            for ph in phases:
-                ph.run()
-            return
-        main_s = torch.cuda.current_stream()
-
-        def launch_decode():
-            side.wait_stream(main_s)
-            with torch.cuda.stream(side):
-                phases[1].run()
-
-        phases[0].run(after_gate_up=launch_decode)
-        main_s.wait_stream(side)
+        run_mixed_step(torch, phases, side)
 
     for _ in range(args.warmup):
         run_step()

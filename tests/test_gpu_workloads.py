@@ -270,3 +270,38 @@ def test_moe64s2_decode_free_running():
     print(f"moe64s2 decode: free-running normwise {err:.2e}, h-code byte flips {flips}")
     if flips == 0:
         assert err <= 1e-3
+
+
+def test_moe64s2_two_streams_match_one_stream():
+    """The benchmark's step runs the decode batch on a second stream beside the prefill
+    batch.  The calls keep no global state and every kernel is deterministic, so each
+    output of both batches must be bit-identical to the one-stream step, on every
+    repetition."""
+    wl, host, W = moe_setup("moe64s2_h2048_f1408")
+    phases = []
+    for T, decode in ((4096, False), (32, True)):
+        x, lg = datagen.moe_tokens(wl, T, decode=decode)
+        ph, _ = run_bench_phase(wl, W, x, lg, decode=decode)
+        phases.append(ph)
+
+    def outputs(ph):
+        d = dict(codes=ph.codes, scales=ph.scales, h=ph.h, codes_h=ph.codes_h,
+                 scales_h=ph.scales_h, out=ph.out, y=ph.y)
+        d.update({"rt_" + k: v for k, v in ph.rt.items() if k != "ws"})
+        return d
+
+    bench.run_mixed_step(torch, phases)
+    torch.cuda.synchronize()
+    ref = [{k: v.clone() for k, v in outputs(ph).items()} for ph in phases]
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        for ph in phases:
+            for v in outputs(ph).values():
+                v.view(torch.uint8).fill_(0xA5)     # stale values must not survive
+        torch.cuda.synchronize()
+        bench.run_mixed_step(torch, phases, side)
+        torch.cuda.synchronize()
+        for i, ph in enumerate(phases):
+            for k, v in outputs(ph).items():
+                assert torch.equal(v.view(torch.uint8), ref[i][k].view(torch.uint8)), \
+                    f"phase {i} output {k} differs on repetition {rep}"
