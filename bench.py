@@ -552,6 +552,55 @@ def bench_kmeans(args, cbq, torch):
     print(json.dumps(line))
 
 
+def bench_peaks(args, torch):
+    """Measured ceilings beside the vendor figures used as roofline peaks: HBM with a
+    plain 1 GiB device copy and a 1 GiB read (a sum), and the fp16/bf16 matrix cores
+    with library GEMMs (torch.matmul, which calls hipBLASLt), at a large square shape
+    and at the 8-expert layer's per-expert shapes (about 128 rows per expert)."""
+    dev = "cuda:0"
+
+    def time_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = time_ms(lambda: dst.copy_(src), 10)
+    read_ms = time_ms(lambda: src.sum(), 10)
+    del src, dst
+    hbm = dict(copy_GBs=round(2 * n / (copy_ms / 1000) / 1e9, 1),
+               read_GBs=round(n / (read_ms / 1000) / 1e9, 1))
+
+    gemms = {}
+    shapes = [("square_8192", 8192, 8192, 8192),
+              ("moe8_gate_up_M128", 128, 4096, 2 * 14336),
+              ("moe8_down_M128", 128, 14336, 4096),
+              ("moe8_gate_up_M1024", 1024, 4096, 2 * 14336)]
+    torch.manual_seed(0)
+    for dt_name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        for name, M, K, N in shapes:
+            a = torch.randn(M, K, device=dev).to(dt)
+            b = torch.randn(K, N, device=dev).to(dt)     # contiguous, no transposed view
+            ms = time_ms(lambda: torch.matmul(a, b), 20)
+            gemms[f"{dt_name}_{name}"] = dict(M=M, K=K, N=N, us=round(ms * 1000, 1),
+                                               TFLOPs=round(2 * M * K * N / (ms / 1000) / 1e12, 1))
+            del a, b
+    line = dict(mode="peaks", hbm=hbm, hbm_vendor_GBs=HBM_PEAK_GBS,
+                hbm_copy_frac_of_vendor=round(hbm["copy_GBs"] / HBM_PEAK_GBS, 3),
+                hbm_read_frac_of_vendor=round(hbm["read_GBs"] / HBM_PEAK_GBS, 3),
+                gemm=gemms, mfma_vendor_TFLOPs=F16_MFMA_PEAK_TFLOPS,
+                note="torch.matmul on ROCm dispatches fp16/bf16 GEMMs to hipBLASLt")
+    print(json.dumps(line))
+
+
 def bench_dense_rotation(args, cbq, torch):
     """The dense-rotation variant of rotate_quantize on the workload's layer input
     (T prefill tokens x H channels, R a seeded H x H stand-in for a learned rotation):
@@ -627,6 +676,9 @@ def main():
     ap.add_argument("--decode-overlap", choices=("down", "serial"), default="down",
                     help="down: the decode batch runs on a second stream, beside the prefill "
                          "batch's down projection; serial: after the prefill batch, on one stream")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the HBM and fp16/bf16 GEMM ceilings with a device copy and "
+                         "library GEMMs instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -664,6 +716,9 @@ def main():
         return
     if args.latency_table:
         bench_latency_table(args, cbq, torch)
+        return
+    if args.peaks:
+        bench_peaks(args, torch)
         return
     if args.dense_rotation:
         bench_dense_rotation(args, cbq, torch)
