@@ -168,19 +168,40 @@ route_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int E, int topk
     if (i / E < c) atomicAdd(&base[e], v);
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] += run;
-      if (c == 0) offsets[e] = run;
-      run += total[e];
+  if (tid < 64) {
+    // exclusive scan of the expert totals by the first wave: lane l holds experts
+    // 4l .. 4l+3 (E <= 256)
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      v[i] = e < E ? total[e] : 0;
+      sum += v[i];
     }
-    if (c == 0) {
-      for (int s = 0; s < n_shared; ++s) {
-        offsets[E + s] = run;
-        run += (int)T;
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (tid >= d) incl += o;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      if (e < E) {
+        base[e] += run;
+        if (c == 0) offsets[e] = run;
       }
-      offsets[E + n_shared] = run;
+      run += v[i];
+    }
+    const int routed = __shfl(incl, 63);   // every routed slot (read by the whole wave)
+    if (c == 0 && tid == 0) {
+      int r = routed;
+      for (int s2 = 0; s2 < n_shared; ++s2) {
+        offsets[E + s2] = r;
+        r += (int)T;
+      }
+      offsets[E + n_shared] = r;
     }
   }
   __syncthreads();
