@@ -161,11 +161,22 @@ route_scatter_kernel(const int32_t* __restrict__ ids, int64_t T, int E, int topk
     base[e] = 0;
   }
   __syncthreads();
-  for (int64_t i = tid; i < (int64_t)nchunks * E; i += nthr) {   // integer sums: order-free
-    const int v = ws[i];
-    const int e = (int)(i % E);
-    atomicAdd(&total[e], v);
-    if (i / E < c) atomicAdd(&base[e], v);
+  {
+    // thread (part p, expert e) sums chunks p, p + parts, ... of expert e in registers,
+    // then adds its two partial sums in LDS (integer sums: the order does not matter)
+    const int parts = nthr / E;   // >= 4 with 1024 threads (E <= 256); the zero-token
+                                  // launch (64 threads) may get 0 but has no chunks
+    if (tid < parts * E) {
+      const int e = tid % E, p = tid / E;
+      int tot = 0, bs = 0;
+      for (int cc = p; cc < nchunks; cc += parts) {
+        const int v = ws[(int64_t)cc * E + e];
+        tot += v;
+        if (cc < c) bs += v;
+      }
+      if (tot) atomicAdd(&total[e], tot);
+      if (bs) atomicAdd(&base[e], bs);
+    }
   }
   __syncthreads();
   if (tid < 64) {
