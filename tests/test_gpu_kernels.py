@@ -102,7 +102,8 @@ def test_rotate_quantize_empty():
 @pytest.mark.parametrize("T,E,k,S,renorm", [(1, 128, 8, 0, True), (64, 128, 8, 0, True),
                                             (512, 8, 2, 0, True), (37, 64, 6, 2, True),
                                             (4096, 64, 6, 2, True), (300, 256, 8, 1, False),
-                                            (2500, 16, 1, 0, True), (5, 4, 4, 0, False)])
+                                            (2500, 16, 1, 0, True), (5, 4, 4, 0, False),
+                                            (3000, 1, 1, 0, True), (65536, 64, 6, 2, True)])
 def test_route_bit_exact(T, E, k, S, renorm):
     lg = datagen.random_logits(T + E + k, T, E)
     lg[0, :min(E, 6)] = np.float32(1.25)                 # a tie
@@ -116,9 +117,10 @@ def test_route_bit_exact(T, E, k, S, renorm):
     assert np.abs(r["weights"].cpu().numpy().astype(np.float64) - ref["weights64"]).max() <= 1e-6
 
 
-def test_route_zero_tokens():
-    r = cbq.moe_route_gather(torch.empty((0, 8), dtype=torch.float32, device=DEV), 2, True, 1)
-    assert r["offsets"].cpu().tolist() == [0] * 10
+@pytest.mark.parametrize("E,k,S", [(8, 2, 1), (256, 8, 2)])
+def test_route_zero_tokens(E, k, S):
+    r = cbq.moe_route_gather(torch.empty((0, E), dtype=torch.float32, device=DEV), k, True, S)
+    assert r["offsets"].cpu().tolist() == [0] * (E + S + 1)
 
 
 # ---------------------------------------------------------------------------
