@@ -283,14 +283,17 @@ static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStrea
 }
 
 hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream) {
-  // enough waves per grid to keep HBM busy: split K (small experts) or rows (large)
+  // Split K (small experts) or rows (large) only while the grid holds fewer than 2,048
+  // waves, and never below four 128-channel chunks per wave.  Measured on the decode
+  // shapes, fewer and longer waves win: a wave's index loads are then spread over more
+  // chunks, and a split costs a reduction through LDS.
   const int E = a.offsets ? a.E : 1;
   const int64_t active = a.offsets ? (a.n_rows < E ? a.n_rows : E) : 1;
   const int ng = decode_groups(a.bits, a.n_w);
   const int64_t tiles = (int64_t)((a.N + 16 * ng - 1) / (16 * ng)) * (active > 0 ? active : 1);
   const int nchunks = (a.K + 127) / 128;
   int splitk = 1;
-  while (splitk < 16 && tiles * splitk < 4096 && splitk * 2 <= nchunks) splitk *= 2;
+  while (splitk < 16 && tiles * splitk < 2048 && splitk * 8 <= nchunks) splitk *= 2;
   if (a.n_w == 2 && splitk > 8) splitk = 8;
   const int ab = a.act_bits;
   switch (a.bits * 10 + (ab == 8 ? 8 : 4)) {
