@@ -601,6 +601,57 @@ def bench_peaks(args, torch):
     print(json.dumps(line))
 
 
+def bench_crossover(args, cbq, torch):
+    """LUT path against MFMA path with the caches flushed, for 16 experts of exactly M
+    rows each, on three matrix shapes of the workloads: where AUTO's row threshold
+    should sit."""
+    dev = "cuda:0"
+    flush = CacheFlush(torch, dev, args.flush)
+
+    def cold_us(fn, reps=8):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e) * 1000.0)
+        ts.sort()
+        return round(sum(ts[1:-1]) / (len(ts) - 2), 1)
+
+    def upw(ws):
+        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
+                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
+                                   K=ws.K, bits=ws.bits)
+
+    E = 16
+    rows = []
+    for (N, K, bits, n_w, label) in ((1408, 2048, 3, 2, "gate/up 3-bit, 64+2-expert layer"),
+                                     (2048, 1408, 2, 1, "down 2-bit, 64+2-expert layer"),
+                                     (768, 2048, 4, 2, "gate/up 4-bit, 128-expert layer")):
+        Ws = [upw(datagen.random_weights(100 + i, E, N, K, bits, keep_raw=False))
+              for i in range(n_w)]
+        for M in (8, 16, 24, 32, 48, 64, 96, 128):
+            T = E * M
+            x = datagen.random_tokens(7, T, K)
+            xt = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            codes, scales = cbq.rotate_quantize(xt, 4)
+            offs = torch.arange(0, T + 1, M, dtype=torch.int32, device=dev)
+            out = torch.empty((T, N), dtype=torch.bfloat16 if n_w == 2 else torch.float32,
+                              device=dev)
+            t = {name: cold_us(lambda: cbq.codebook_lut_gemm(codes, scales, 4, Ws,
+                                                             expert_offsets=offs, path=p,
+                                                             out=out))
+                 for name, p in (("lut_us", cbq.PATH_LUT), ("mfma_us", cbq.PATH_MFMA))}
+            rows.append(dict(shape=label, N=N, K=K, bits=bits, experts=E, rows_per_expert=M, **t))
+    print(json.dumps(dict(mode="crossover", auto_max_lut_rows=cbq.AUTO_MAX_LUT_ROWS,
+                          cache_flush=args.flush, results=rows)))
+
+
 def bench_dense_rotation(args, cbq, torch):
     """The dense-rotation variant of rotate_quantize on the workload's layer input
     (T prefill tokens x H channels, R a seeded H x H stand-in for a learned rotation):
@@ -676,6 +727,8 @@ def main():
     ap.add_argument("--decode-overlap", choices=("down", "serial"), default="down",
                     help="down: the decode batch runs on a second stream, beside the prefill "
                          "batch's down projection; serial: after the prefill batch, on one stream")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the LUT and MFMA paths against rows per expert instead")
     ap.add_argument("--peaks", action="store_true",
                     help="measure the HBM and fp16/bf16 GEMM ceilings with a device copy and "
                          "library GEMMs instead")
@@ -719,6 +772,9 @@ def main():
         return
     if args.peaks:
         bench_peaks(args, torch)
+        return
+    if args.crossover:
+        bench_crossover(args, cbq, torch)
         return
     if args.dense_rotation:
         bench_dense_rotation(args, cbq, torch)
