@@ -383,8 +383,7 @@ def bench_latency_table(args, cbq, torch):
     times the K-means clustering error of synthetic bf16 weights at that width, built on
     the GPU) gives the error; the allocation minimises the summed error within the
     latency of a uniform 3-bit layer."""
-    from codebook_bit_quantized_amd.allocation import allocate_bits, clustering_error
-    import oracle
+    from codebook_bit_quantized_amd.allocation import allocate_bits, clustering_errors, route_share
     wl = datagen.WORKLOADS[args.workload]
     dev = "cuda:0"
     E = wl.E + wl.n_shared
@@ -433,11 +432,12 @@ def bench_latency_table(args, cbq, torch):
         del G, U, D
     del flush
 
-    # importance: share of the routed prefill tokens per expert (shared experts: all)
+    # importance: share of the routed prefill tokens per expert (shared experts: all),
+    # from the library's own routing of the prefill batch
     xp, lgp = datagen.moe_tokens(wl, wl.T_list[0])
-    counts = oracle.route(lgp, wl.topk, True, wl.n_shared)["counts"].astype(np.float64)
-    share = np.concatenate([counts / wl.T_list[0], np.ones(wl.n_shared)])
-    # clustering error per matrix and width on a sample of synthetic bf16 weight rows
+    share = route_share(cbq, torch.from_numpy(lgp).to(dev), wl.topk, wl.n_shared)
+    # clustering error per matrix and width on a sample of synthetic bf16 weight rows,
+    # clustered on the GPU and decoded by the allocation module
     rows = 64
     kinds = (("gate", wl.F, wl.H), ("up", wl.F, wl.H), ("down", wl.H, wl.F))
     err = np.zeros((E * 3, len(choices)))
@@ -445,16 +445,10 @@ def bench_latency_table(args, cbq, torch):
     for m, (name, N, K) in enumerate(kinds):
         w_np = np.concatenate([datagen.weights_bf16(wl.wid, datagen.TAG_W_FULL, 3 * e + m, rows, K)
                                for e in range(E)])
-        wf = oracle.bf16_bits_to_f64(w_np)
-        w = torch.from_numpy(w_np.view(np.int16)).to(dev)
+        sq = clustering_errors(cbq, torch, w_np, E, choices, 30, dev)
+        err[3 * np.arange(E) + m, :] = share[:, None] * sq * (N / rows)
+        key = "decode_down_us" if name == "down" else "decode_gate_up_us"
         for c, bits in enumerate(choices):
-            cw = cbq.kmeans_codebooks(w, bits, 30)
-            idx = oracle.unpack_indices(cw.idx[0].cpu().numpy(), K, bits)
-            cbk = oracle.f16_bits_to_f64(cw.codebook[0].cpu().numpy().view(np.uint16))
-            for e in range(E):
-                sl = slice(e * rows, (e + 1) * rows)
-                err[3 * e + m, c] = share[e] * clustering_error(wf[sl], cbk[sl], idx[sl]) * (N / rows)
-            key = "decode_down_us" if name == "down" else "decode_gate_up_us"
             lat[3 * np.arange(E) + m, c] = table[bits][key] / E / (1 if name == "down" else 2)
     budget = float(lat[:, 1].sum()) * 1.01      # a uniform 3-bit layer (+1 %: latency grid slack)
     bits = allocate_bits(lat, err, budget)

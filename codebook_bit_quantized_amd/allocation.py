@@ -62,8 +62,67 @@ def allocate_bits(latency: np.ndarray, error: np.ndarray, budget: float, choices
     return out
 
 
-def clustering_error(w_rows: np.ndarray, codebook: np.ndarray, idx: np.ndarray) -> float:
-    """Sum of squared differences between weight rows (float [R][K]) and their
-    dequantised codebook approximation (codebook float [R][L], idx int [R][K])."""
-    approx = np.take_along_axis(codebook, idx, axis=1)
-    return float(np.square(w_rows - approx).sum())
+# ---------------------------------------------------------------------------
+# Inputs of the allocation, computed from the library's own results: routing counts
+# from cbq_moe_route_gather and clusterings from cbq_kmeans_codebooks, decoded here.
+
+def unpack_indices(packed: np.ndarray, K: int, bits: int) -> np.ndarray:
+    """Indices [..., K] (int64) of rows stored as the cbq_weights bitstream [..., K*bits/8]:
+    index k occupies bits [k*bits, (k+1)*bits) counted from bit 0 of byte 0 (bits <= 4,
+    so an index spans at most two bytes)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lead = p.shape[:-1]
+    rows = p.reshape(-1, p.shape[-1]).astype(np.uint16)
+    rows = np.concatenate([rows, np.zeros((rows.shape[0], 1), dtype=np.uint16)], axis=1)
+    start = np.arange(K, dtype=np.int64) * bits
+    byte, shift = start >> 3, (start & 7).astype(np.uint16)
+    pair = rows[:, byte] | (rows[:, byte + 1] << np.uint16(8))
+    out = (pair >> shift) & np.uint16((1 << bits) - 1)
+    return out.astype(np.int64).reshape(*lead, K)
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 (a bf16 value is the high half of an fp32)."""
+    return (np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns -> float64."""
+    return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def expert_share(offsets: np.ndarray, T: int, n_routed: int, n_shared: int) -> np.ndarray:
+    """Importance proxy per expert from the router's row offsets [E + S + 1]: the share of
+    the T tokens routed to each of the E routed experts, and 1 for each shared expert
+    (they see every token)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    counts = np.diff(off[:n_routed + 1]).astype(np.float64)
+    return np.concatenate([counts / float(T), np.ones(n_shared)])
+
+
+def route_share(cbq, logits, topk: int, n_shared: int) -> np.ndarray:
+    """expert_share of the routing that cbq.moe_route_gather gives device logits [T][E]."""
+    T, E = int(logits.shape[0]), int(logits.shape[1])
+    rt = cbq.moe_route_gather(logits, topk, True, n_shared)
+    return expert_share(rt["offsets"].cpu().numpy(), T, E, n_shared)
+
+
+def clustering_errors(cbq, torch, w_bits: np.ndarray, groups: int, choices: Sequence[int] = (2, 3, 4),
+                      max_iters: int = 30, device: str = "cuda:0") -> np.ndarray:
+    """Per-row K-means (cbq.kmeans_codebooks, on the GPU) of bf16 rows w_bits [groups*r][K]
+    at every width in choices; returns [groups][len(choices)], the summed squared
+    clustering error of each group of r consecutive rows."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    R, K = w_bits.shape
+    if R % groups:
+        raise ValueError("rows must split evenly into groups")
+    wf = bf16_bits_to_float(w_bits)
+    w = torch.from_numpy(w_bits.view(np.int16)).to(device)
+    out = np.zeros((groups, len(choices)))
+    for c, bits in enumerate(choices):
+        cw = cbq.kmeans_codebooks(w, bits, max_iters)
+        idx = unpack_indices(cw.idx.reshape(R, -1).cpu().numpy(), K, bits)
+        cb = f16_bits_to_float(cw.codebook.reshape(R, -1).cpu().numpy().view(np.uint16))
+        sq = np.square(wf - np.take_along_axis(cb, idx, axis=1)).sum(axis=1)
+        out[:, c] = sq.reshape(groups, -1).sum(axis=1)
+    return out

@@ -1,8 +1,8 @@
 // Device-side building blocks shared by the GEMM kernels (gfx950, wave64).
 //
 // Per-row codebook tables live in VGPRs and are looked up with v_perm_b32 byte
-// permutes, so the "one-time LUT precomputation then lookup" of the LUT kernel
-// (CodeQuant2, Figure 4) costs no LDS bandwidth and has no bank conflicts (the
+// permutes, so the table the LUT kernel builds once and then reads (CodeQuant2,
+// Figure 4) costs no LDS bandwidth and has no bank conflicts (the
 // problem the AI Radio episode's "Improvements" section describes for an
 // LDS-resident table).
 //
@@ -233,14 +233,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, ((uint32_t)h) << 16);
 }
 
-// g * u / (1 + exp(-g)) in fp32
+// SiLU(g) * u in fp32 for the SwiGLU epilogue of every GEMM path: g * u * rcp(1 + exp(-g))
+// with the hardware exp2 (of -g * log2 e) and reciprocal, each within a few fp32 ulps.
+// The result is rounded to bf16 (2^16 fp32 ulps apart), so it lies within one bf16 step
+// of the exactly rounded value.  Both GEMM paths call this one function, so equal fp32
+// (g, u) give equal bf16 h whichever path computed them.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g * u / (1.0f + expf(-g));
-}
-
-// Same with the hardware exp2 and reciprocal (a few ulp in fp32; the result is then
-// rounded to bf16, whose spacing is 2^16 fp32 ulps).
-__device__ __forceinline__ float silu_mul_fast(float g, float u) {
   return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 

@@ -2,8 +2,8 @@
 //
 // Once an expert has enough rows, every dequantised weight is reused by many tokens
 // and the work becomes MFMA-bound.  Weights are dequantised with the same per-row
-// register tables as the decode path (CodeQuant2, Figure 4: a one-time table
-// precomputation followed by lookups), and go straight into the B operand of
+// register tables as the decode path (CodeQuant2, Figure 4: a table built once, then
+// read instead of multiplying), and go straight into the B operand of
 // 32x32x16 fp16 MFMAs: the 32 consecutive indices one lane loads per 64-channel step
 // are exactly the 4 x 8 values its B fragments need, so weights never pass through
 // LDS.  Activation codes are converted to fp16 once per step into LDS and shared by
@@ -209,7 +209,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
         for (int j = 0; j < 4; ++j) {
           const int v = 4 * q + j;
           const float gv = acc[ms][0][v] * sc[j], uv = acc[ms][1][v] * sc[j];
-          hb[j] = f32_to_bf16_rne(silu_mul_fast(gv, uv));
+          hb[j] = f32_to_bf16_rne(silu_mul(gv, uv));
         }
         const bool odd = (nl & 1) != 0;
 #pragma unroll

@@ -16,8 +16,8 @@
 //
 // Optionally, before the rotation, each channel is multiplied by an fp32 smoothing
 // factor (one fp32 rounding; the exactness bound then becomes 29 - log2(b) binades)
-// and/or negated by a random sign bit (CodeQuant2, Figure 1: rotation and scaling
-// fused for outlier smoothing; Table 5 caption: a fixed random rotation with
+// and/or negated by a random sign bit (CodeQuant2, Figure 1: per-channel scales and a
+// rotation folded into the weights smooth the outliers; Table 5 caption: a fixed random rotation with
 // SmoothQuant scaling).
 //
 // The quantiser follows one fixed IEEE fp32 sequence: v = fp32(u), M = max|v|,

@@ -54,7 +54,9 @@ enum {
   CBQ_PATH_LUT = 1,   /* register codebook lookup feeding 16x16x32 MFMA; an expert's weights
                          are streamed from HBM once (K split over waves for experts of at most
                          32 rows, row blocks of 32 split over waves for larger ones) */
-  CBQ_PATH_MFMA = 2   /* weights dequantised tile by tile into LDS as fp16, 32x32x16 MFMA */
+  CBQ_PATH_MFMA = 2   /* 256-row tiles: weights dequantised in registers straight into the
+                         B operand of 32x32x16 fp16 MFMAs, activation codes converted to fp16
+                         once per tile step in LDS */
 };
 
 #define CBQ_AUTO_MAX_LUT_ROWS 32
@@ -107,9 +109,9 @@ int cbq_rotate_quantize(const uint16_t* x, int64_t T, int32_t K, int64_t ldx,
 
 /*
  * cbq_rotate_quantize_ex - cbq_rotate_quantize with per-channel transforms before the
- * rotation.  Passage: CodeQuant2, Figure 1 (rotation and scaling fused into the model
- * for outlier smoothing) and Table 5 caption (the base configuration: a fixed random
- * rotation with SmoothQuant scaling).
+ * rotation.  Passage: CodeQuant2, Figure 1 (per-channel scales and a rotation, folded
+ * into the weights, smooth the activation outliers) and Table 5 caption (the base
+ * setting is a fixed random rotation with SmoothQuant scaling).
  *
  *  smooth : optional fp32 [K] multipliers m (16-byte aligned): channel c becomes
  *           fp32(x_c * m_c), one fp32 rounding (a SmoothQuant factor 1/s_c).
@@ -187,8 +189,8 @@ int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk
 
 /*
  * cbq_codebook_lut_gemm - grouped expert GEMM with codebook weights.
- * Passage: CodeQuant2, Figure 4 (LUT kernel: a one-time table precomputation, then
- * table lookups from on-chip memory) and Figure 3 (per-row centroid codebooks); the
+ * Passage: CodeQuant2, Figure 4 (the kernel builds a table once, then reads products
+ * from on-chip memory instead of multiplying) and Figure 3 (per-row centroid codebooks); the
  * AI Radio episode, "Improvements" (products looked up instead of recomputed;
  * shared-memory bank conflicts).
  *
@@ -199,15 +201,26 @@ int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk
  *                    R rows use expert 0.
  *  row_token       : int32 [R]: row r reads token row_token[r] of codes/scales
  *                    (sorted_tokens of the router), or NULL: row r reads token r.
+ *                    Every entry of a row inside an expert range must lie in [0, T),
+ *                    T the number of token rows of codes and scales.  The call is not
+ *                    told T, so it cannot check this: an entry outside that range
+ *                    makes the kernels read outside codes and scales (caller's
+ *                    contract, like the extents of every other buffer).
  *  W, n_w          : n_w == 1: one weight set; n_w == 2: {gate, up} with equal
  *                    E/N/K/bits (host pointer to the array; read during the call only).
  *  epilogue        : CBQ_EPI_F32 (n_w == 1): out[r][n] = scale[t_r] * sum_k q[t_r][k] W[e][n][k]
  *                    as fp32.  CBQ_EPI_SWIGLU_BF16 (n_w == 2): g, u as above, then
  *                    out[r][n] = bf16_rne(silu(g) * u).
- *  path            : CBQ_PATH_AUTO / CBQ_PATH_LUT / CBQ_PATH_MFMA (results agree within
- *                    fp32 accumulation order; products are exact in every path).
+ *  path            : CBQ_PATH_AUTO / CBQ_PATH_LUT / CBQ_PATH_MFMA.  Products are exact
+ *                    on every path; the paths differ only in the fp32 summation order.
+ *                    The SwiGLU epilogue is one fp32 formula on every path
+ *                    (g * u * rcp(1 + exp(-g)) with the hardware exp2 and reciprocal),
+ *                    so the bf16 h of two paths differs only where that summation
+ *                    order moves g or u across a bf16 rounding boundary: by one bf16
+ *                    step at most.
  *  out, ldo        : fp32 or bf16 [R][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
- *  ws, ws_bytes    : workspace of at least cbq_gemm_workspace(...) bytes.
+ *  ws, ws_bytes    : workspace of at least cbq_gemm_workspace(...) bytes.  The GEMM
+ *                    kernels need none: cbq_gemm_workspace returns 0 and ws may be NULL.
  *  Rows of experts with no rows, and rows outside every expert range, are not written.
  *  Limits (CBQ_EUNSUPPORTED beyond them): the output is smaller than 1 GiB, one
  *  expert's index block and the codes array are smaller than 2 GiB each (the codes

@@ -3,19 +3,19 @@
 Sources (cited by page title and the section / figure on it):
 
 * CodeQuant2 - "Enhanced Outlier Mitigation and Adaptive Clustering for Low-Precision
-  LRMs" (abstract; Figure 1: rotation and scaling are fused into the model for outlier
-  smoothing and the model runs a LUT-based kernel; Figure 3 right: a centroid matrix
-  plus per-row binary assignment matrices, i.e. one codebook per weight row; Figure 4:
-  the LUT kernel is a one-time LUT precomputation followed by table lookups, with the
-  table held in on-chip shared memory; Tables 1 and 9: the A4W4 and A8W4 settings;
-  Table 5 caption: the base configuration uses a fixed rotation and SmoothQuant
-  scaling).
+  LRMs" (abstract; Figure 1: the outlier-smoothing rotation and per-channel scales are
+  folded into the weights, and inference runs a table-lookup kernel; Figure 3 right: a
+  centroid matrix plus per-row binary assignment matrices, i.e. one codebook per weight
+  row; Figure 4: the kernel builds its table once and then reads products from it
+  instead of multiplying, the table sitting in on-chip shared memory; Tables 1 and 9:
+  the A4W4 and A8W4 settings; Table 5 caption: the base configuration pairs a fixed
+  rotation with SmoothQuant scaling).
 * CodeQuant - "Unified Clustering and Quantization for Enhanced Outlier Smoothing in
   Low-Precision Mixture-of-Experts" (abstract: rotation smooths activation outliers,
   weight outliers are absorbed into cluster centroids, MoE models, dedicated LUT
   kernels); the AI Radio episode on the same paper (introduction: a router sends each
   input to an expert; "Improvements": the kernel precomputes products and looks them
-  up like a multiplication table; shared-memory bank conflicts).
+  up rather than recomputed; shared-memory bank conflicts).
 
 Readings taken where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -186,8 +186,9 @@ def rotate(x_bits: np.ndarray, b: int) -> Tuple[np.ndarray, np.ndarray]:
 def smooth_and_sign(x_bits: np.ndarray, smooth: Optional[np.ndarray] = None,
                     signs: Optional[np.ndarray] = None) -> Tuple[np.ndarray, int]:
     """The per-channel transforms applied before the Hadamard blocks (CodeQuant2,
-    Figure 1: rotation and scaling fused for outlier smoothing; Table 5 caption: a fixed
-    random rotation with SmoothQuant scaling).
+    Figure 1: per-channel scales and a rotation, both folded into the weights, smooth the
+    activation outliers; Table 5 caption: the base setting is a fixed random rotation
+    with SmoothQuant scaling).
 
     v_c = fp32(x_c * m_c) with fp32 multipliers m (one rounding; skipped when smooth is
     None), negated where bit c of the LSB-first bitmask signs is set.  Returns (v as

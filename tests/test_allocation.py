@@ -56,3 +56,32 @@ def test_budget_below_fastest_raises():
     lat = np.array([[1.0, 2.0, 3.0]])
     with pytest.raises(ValueError):
         allocate_bits(lat, np.zeros((1, 3)), 0.5)
+
+
+def test_library_index_decoding_matches_the_oracle():
+    # the allocation inputs decode the library's clusterings with their own helpers;
+    # the oracle's bit unpacking and fp16 / bf16 conversions are the reference
+    import oracle
+    from codebook_bit_quantized_amd.allocation import (bf16_bits_to_float, f16_bits_to_float,
+                                                       unpack_indices)
+    g = np.random.default_rng(5)
+    for bits in (2, 3, 4):
+        for K in (32, 96, 1408):
+            p = g.integers(0, 256, (2, 3, K * bits // 8), dtype=np.uint8)
+            assert np.array_equal(unpack_indices(p, K, bits), oracle.unpack_indices(p, K, bits))
+    h = g.integers(0, 1 << 16, 4096, dtype=np.uint16)
+    h = h[(h & 0x7C00) != 0x7C00]                      # finite fp16 patterns
+    assert np.array_equal(f16_bits_to_float(h), oracle.f16_bits_to_f64(h))
+    b = g.integers(0, 1 << 16, 4096, dtype=np.uint16)
+    b = b[(b & 0x7F80) != 0x7F80]                      # finite bf16 patterns
+    assert np.array_equal(bf16_bits_to_float(b), oracle.bf16_bits_to_f64(b))
+
+
+def test_expert_share_from_offsets():
+    from codebook_bit_quantized_amd.allocation import expert_share
+    import oracle
+    lg = np.random.default_rng(3).standard_normal((40, 8)).astype(np.float32)
+    rt = oracle.route(lg, 2, True, 1)
+    share = expert_share(rt["offsets"], 40, 8, 1)
+    assert np.array_equal(share[:8], rt["counts"] / 40.0)
+    assert share[8] == 1.0 and share[:8].sum() == 2.0   # top-2: every token counted twice

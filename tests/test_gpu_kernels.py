@@ -224,6 +224,36 @@ def test_many_tile_decode_gemm(bits, act_bits, n_w, path):
         assert_normwise(out.cpu().numpy(), ref[0], 1e-3, "f32")
 
 
+@pytest.mark.parametrize("bits,act_bits", [(3, 4), (4, 8)])
+def test_swiglu_paths_agree(bits, act_bits):
+    """Both GEMM paths end in the same SwiGLU formula; only the fp32 summation order of g
+    and u differs.  So on the same rows the bf16 h of the LUT and MFMA paths is equal or
+    one bf16 step apart (where g or u moved across a rounding midpoint), and AUTO gives,
+    bit for bit, the LUT result for experts of at most 32 rows and the MFMA result for
+    the others."""
+    T, E, k, S, H, F = 120, 8, 2, 1, 512, 320
+    wl, gate, up, down, x, lg = _moe_case(90 + bits, T, E, k, S, H, F, bits, act_bits)
+    rq = oracle.rotate_quantize(x, 0, act_bits)
+    rt = oracle.route(lg, k, True, S)
+    G, U = upload_weights(gate), upload_weights(up)
+    args = (to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits, [G, U])
+    kw = dict(expert_offsets=to_dev(rt["offsets"]), row_token=to_dev(rt["sorted_tokens"]))
+    h = {p: bf16_to_bits(cbq.codebook_lut_gemm(*args, path=p, **kw))
+         for p in (cbq.PATH_LUT, cbq.PATH_MFMA, cbq.PATH_AUTO)}
+    a = h[cbq.PATH_LUT].astype(np.int32)
+    b = h[cbq.PATH_MFMA].astype(np.int32)
+    same_sign = (a ^ b) & 0x8000 == 0
+    step = np.where(same_sign, np.abs(a - b), np.abs((a & 0x7FFF) + (b & 0x7FFF)))
+    assert step.max() <= 1, f"LUT and MFMA h differ by {step.max()} bf16 steps"
+    print(f"bits={bits} A{act_bits}: h equal on both paths for {np.mean(step == 0):.5f} of values")
+    counts = np.diff(rt["offsets"])
+    assert counts.min() <= cbq.AUTO_MAX_LUT_ROWS < counts.max()      # both paths taken
+    for e in range(E + S):
+        r0, r1 = rt["offsets"][e], rt["offsets"][e + 1]
+        want = h[cbq.PATH_LUT] if r1 - r0 <= cbq.AUTO_MAX_LUT_ROWS else h[cbq.PATH_MFMA]
+        assert np.array_equal(h[cbq.PATH_AUTO][r0:r1], want[r0:r1]), e
+
+
 def test_gemm_deterministic():
     wl, gate, up, down, x, lg = _moe_case(7, 200, 8, 2, 1, 256, 192, 4, 4)
     rq = oracle.rotate_quantize(x, 0, 4)

@@ -214,6 +214,20 @@ def test_moe128_decode_layer(T):
     check_moe_phase(wl, host, ph, x, lg, seed=100 + T, extra_paths=(cbq.PATH_MFMA,))
 
 
+def _flips(ph, ref):
+    """h-code bytes that differ from the free-running oracle, and the bound they are held
+    to.  A GPU h value differs from the exactly rounded one only when its fp32 value
+    (fp32 sums, hardware exp2 and reciprocal: a relative error of about 1e-6) lands on
+    the other side of a bf16 rounding midpoint, for about 5e-4 of the values.  Such a
+    one-step change moves the codes of its 128-channel block by under 1e-3 of a
+    quantisation step, so it flips a code with probability about 2e-3: roughly 1e-4 of
+    the codes flip.  The bound is 1e-4 of the codes (two per byte for A4), at least 4."""
+    got = ph.codes_h.cpu().numpy()
+    flips = int((got != ref["rqh"]["codes"]).sum())
+    n_codes = got.size * (8 // 4 if ph.wl.act_bits == 4 else 1)
+    return flips, max(4, int(1e-4 * n_codes))
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_moe128_free_running(T):
     """Oracle end to end from x (no teacher forcing) on the small decode batches."""
@@ -222,9 +236,11 @@ def test_moe128_free_running(T):
     ph, _ = run_bench_phase(wl, W, x, lg, decode=True)
     ref = oracle.moe_layer(x, lg, host["gate"], host["up"], host["down"], wl.topk, wl.n_shared,
                            wl.act_bits)
-    flips = int((ph.codes_h.cpu().numpy() != ref["rqh"]["codes"]).sum())
+    flips, bound = _flips(ph, ref)
     err = assert_normwise(ph.y.cpu().numpy(), ref["y"], 2e-2, "free-running y")
-    print(f"moe128 T={T}: free-running normwise {err:.2e}, h-code byte flips {flips}")
+    print(f"moe128 T={T}: free-running normwise {err:.2e}, h-code byte flips {flips} "
+          f"(bound {bound})")
+    assert flips <= bound
     if flips == 0:
         assert err <= 1e-3
 
@@ -265,9 +281,11 @@ def test_moe64s2_decode_free_running():
     ph, _ = run_bench_phase(wl, W, x, lg, decode=True)
     ref = oracle.moe_layer(x, lg, host["gate"], host["up"], host["down"], wl.topk, wl.n_shared,
                            wl.act_bits)
-    flips = int((ph.codes_h.cpu().numpy() != ref["rqh"]["codes"]).sum())
+    flips, bound = _flips(ph, ref)
     err = assert_normwise(ph.y.cpu().numpy(), ref["y"], 2e-2, "free-running y")
-    print(f"moe64s2 decode: free-running normwise {err:.2e}, h-code byte flips {flips}")
+    print(f"moe64s2 decode: free-running normwise {err:.2e}, h-code byte flips {flips} "
+          f"(bound {bound})")
+    assert flips <= bound
     if flips == 0:
         assert err <= 1e-3
 

@@ -80,3 +80,56 @@ def test_power_of_two_calibration_scale_changes_nothing():
     a = oracle.refit_codebooks(w, idx, cb, X)
     X4 = _bf16(datagen.bf16_bits_to_f32(X) * 4.0)
     assert np.array_equal(a, oracle.refit_codebooks(w, idx, cb, X4))
+
+
+def _clustered(R=4, K=64, bits=2, seed=7):
+    w = datagen.weights_bf16(seed, datagen.TAG_W_FULL, 0, R, K)
+    idx, cb, _ = oracle.kmeans_codebooks(w, bits, 20)
+    return w, idx, cb
+
+
+def test_output_error_identity_calibration_is_the_weight_error():
+    # X = I: ||X (W - W_hat)^T||_F / ||X W^T||_F = ||W - W_hat||_F / ||W||_F, a sum of
+    # squares over the weights written out with plain loops
+    w, idx, cb = _clustered()
+    R, K = w.shape
+    wf = oracle.bf16_bits_to_f64(w)
+    cf = oracle.f16_bits_to_f64(cb)
+    num = den = 0.0
+    for r in range(R):
+        for k in range(K):
+            d = wf[r, k] - cf[r, idx[r, k]]
+            num += d * d
+            den += wf[r, k] * wf[r, k]
+    want = (num / den) ** 0.5
+    got = oracle.output_error(w, idx, cb, _bf16(np.eye(K)))
+    assert abs(got - want) <= 1e-12 * want
+
+
+def test_output_error_one_hot_token_selects_a_column():
+    # one calibration token e_j: the error of column j of W alone (Euclidean norm over rows)
+    w, idx, cb = _clustered(seed=8)
+    R, K = w.shape
+    wf = oracle.bf16_bits_to_f64(w)
+    cf = oracle.f16_bits_to_f64(cb)
+    for j in (0, 5, K - 1):
+        x = np.zeros((1, K))
+        x[0, j] = 1.0
+        col = wf[:, j]
+        err = np.array([wf[r, j] - cf[r, idx[r, j]] for r in range(R)])
+        want = np.sqrt((err ** 2).sum()) / np.sqrt((col ** 2).sum())
+        got = oracle.output_error(w, idx, cb, _bf16(x))
+        assert abs(got - want) <= 1e-12 * want, j
+
+
+def test_output_error_hand_example():
+    # W = [[1, 2]], centroids (1, 1.5), assignments (0, 1): W_hat = [[1, 1.5]].
+    # X = [[1, 1], [2, 0]]: X W^T = (3, 2), X (W - W_hat)^T = (0.5, 0):
+    # error = 0.5 / sqrt(13).  A Frobenius norm of W - W_hat alone would give 0.5/sqrt(5).
+    w = _bf16([[1.0, 2.0]])
+    cb = oracle.round_f64_to_f16_bits(np.array([[1.0, 1.5]]))
+    idx = np.array([[0, 1]])
+    X = _bf16([[1.0, 1.0], [2.0, 0.0]])
+    assert oracle.output_error(w, idx, cb, X) == 0.5 / np.sqrt(13.0)
+    # zero error when every weight sits on its centroid
+    assert oracle.output_error(w, idx, oracle.round_f64_to_f16_bits(np.array([[1.0, 2.0]])), X) == 0.0

@@ -209,3 +209,23 @@ def test_code_packing_literals_and_round_trip():
     assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(q4, 4), 64, 4), q4)
     q8 = rng.integers(-127, 128, size=(3, 64)).astype(np.int8)
     assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(q8, 8), 64, 8), q8)
+
+
+# The rotation block of every layer width the workloads use: the largest power of two
+# dividing K (a width with no Sylvester Hadamard matrix of its own is rotated in
+# blocks of that size), and K itself for a power of two.  Values written out by hand.
+@pytest.mark.parametrize("K, b", [(2560, 512), (9728, 512), (768, 256), (14336, 2048),
+                                  (1408, 128), (256, 256), (2048, 2048), (4096, 4096),
+                                  (96, 32), (32, 32)])
+def test_block_size_literals(K, b):
+    assert oracle.block_size(K) == b
+    assert K % b == 0 and (K // b) % 2 == 1       # no larger power of two divides K
+
+
+def test_block_size_override():
+    assert oracle.block_size(2560, 1) == 1          # no rotation
+    assert oracle.block_size(2560, 256) == 256
+    assert oracle.block_size(2048, 2048) == 2048
+    for bad in (3, 1024, 4096, -2):                 # not a power of two dividing K
+        with pytest.raises(ValueError):
+            oracle.block_size(2560, bad)

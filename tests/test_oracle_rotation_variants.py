@@ -1,7 +1,7 @@
 """Pins for the oracle's rotation variants (CPU only): per-channel smoothing scales and
-random signs applied before the Hadamard blocks (CodeQuant2, Figure 1: rotation and
-scaling fused for outlier smoothing; Table 5 caption: a fixed random rotation with
-SmoothQuant scaling).
+random signs applied before the Hadamard blocks (CodeQuant2, Figure 1: per-channel
+scales and a rotation folded into the weights smooth the activation outliers; Table 5
+caption: the base setting is a fixed random rotation with SmoothQuant scaling).
 
 The smoothed values are tied to an independent rounding of the exact products, a sign
 flip to its exact effect on the rotation, one-hot tokens to a closed form, and blocks
