@@ -25,6 +25,7 @@ AUTO_MAX_LUT_ROWS = 32
 # every symbol include/cbq.h declares
 EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_rotate_dense_workspace",
             "cbq_rotate_quantize_dense", "cbq_route_workspace", "cbq_moe_route_gather",
+            "cbq_moe_route_gather_noalloc",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
             "cbq_kmeans_codebooks", "cbq_refit_codebooks", "cbq_cpu_lut_gemm", "cbq_status_string", "cbq_last_error",
             "cbq_version")
@@ -65,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "cbq_route_workspace": (sz, [i64, i32, i32, i32]),
         "cbq_moe_route_gather": (ctypes.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                 vp, sz, vp]),
+        "cbq_moe_route_gather_noalloc": (ctypes.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp,
+                                                        vp, vp, vp]),
         "cbq_gemm_workspace": (sz, [W, i32, i64, i32, i32]),
         "cbq_codebook_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, vp, vp, W, i32, i32, i32, vp,
                                                  i64, vp, sz, vp]),
@@ -215,6 +218,33 @@ def moe_route_gather(logits: torch.Tensor, topk: int, renormalize: bool = True, 
     _check(lib.cbq_moe_route_gather(_ptr(logits), T, E, topk, int(bool(renormalize)), n_shared,
                                     _ptr(ids), _ptr(w), _ptr(offs), _ptr(st), _ptr(so),
                                     _ptr(ws) if need > 0 else None, need, _stream(stream)))
+    return dict(ids=ids, weights=w, offsets=offs, sorted_tokens=st[:R], slot_of=so)
+
+
+def moe_route_gather_noalloc(logits: torch.Tensor, topk: int, renormalize: bool = True,
+                             n_shared: int = 0, out: Optional[dict] = None, stream=None) -> dict:
+    """moe_route_gather through cbq_moe_route_gather_noalloc: the library's own scratch
+    replaces the workspace.  ``out`` may hold preallocated outputs as for
+    moe_route_gather (its "ws" entry is ignored)."""
+    lib = load_library()
+    _require_gpu(logits)
+    T, E = logits.shape
+    dev = logits.device
+    o = out or {}
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        return t if t is not None else torch.empty(shape, dtype=dtype, device=dev)
+
+    R = T * topk + n_shared * T
+    ids = get("ids", (T, topk), torch.int32)
+    w = get("weights", (T, topk), torch.float32)
+    offs = get("offsets", (E + n_shared + 1,), torch.int32)
+    st = get("sorted_tokens", (max(R, 1),), torch.int32)
+    so = get("slot_of", (T, topk), torch.int32)
+    _check(lib.cbq_moe_route_gather_noalloc(_ptr(logits), T, E, topk, int(bool(renormalize)),
+                                            n_shared, _ptr(ids), _ptr(w), _ptr(offs), _ptr(st),
+                                            _ptr(so), _stream(stream)))
     return dict(ids=ids, weights=w, offsets=offs, sorted_tokens=st[:R], slot_of=so)
 
 

@@ -150,6 +150,34 @@ CBQ_EXPORT int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, i
   return CBQ_OK;
 }
 
+CBQ_EXPORT int cbq_moe_route_gather_noalloc(const float* logits, int64_t T, int32_t E, int32_t topk,
+                                            int32_t renormalize, int32_t n_shared,
+                                            int32_t* topk_ids, float* topk_w,
+                                            int32_t* expert_offsets, int32_t* sorted_tokens,
+                                            int32_t* slot_of, void* stream) {
+  g_err[0] = 0;
+  if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
+  if (T > (1 << 24)) return fail(CBQ_EUNSUPPORTED, "T must be <= 2^24");
+  if (E < 1 || E > 256) return fail(CBQ_EUNSUPPORTED, "E must be in [1, 256] (got %d)", E);
+  if (topk < 1 || topk > 8 || topk > E) return fail(CBQ_EINVAL, "topk must be in [1, min(E, 8)] (got %d)", topk);
+  if (n_shared < 0 || n_shared > 8) return fail(CBQ_EINVAL, "n_shared must be in [0, 8] (got %d)", n_shared);
+  if (renormalize != 0 && renormalize != 1) return fail(CBQ_EINVAL, "renormalize must be 0 or 1");
+  if (!expert_offsets) return fail(CBQ_EINVAL, "expert_offsets must be non-null");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_tokens || !slot_of))
+    return fail(CBQ_EINVAL, "logits, topk_ids, topk_w, sorted_tokens and slot_of must be non-null");
+  const size_t need = cbq::route_workspace_bytes(T, E);
+  if (need > cbq::route_scratch_bytes())
+    return fail(CBQ_EUNSUPPORTED, "routing needs %zu bytes of scratch, above the library's %zu",
+                need, cbq::route_scratch_bytes());
+  int32_t* scratch = nullptr;
+  hipError_t e = cbq::route_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_gather_noalloc scratch lookup");
+  e = cbq::launch_route(logits, T, E, topk, renormalize, n_shared, topk_ids, topk_w, expert_offsets,
+                        sorted_tokens, slot_of, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_gather_noalloc launch");
+  return CBQ_OK;
+}
+
 CBQ_EXPORT size_t cbq_gemm_workspace(const cbq_weights* W, int32_t n_w, int64_t n_rows,
                                      int32_t act_bits, int32_t path) {
   (void)W; (void)n_w; (void)n_rows; (void)act_bits; (void)path;

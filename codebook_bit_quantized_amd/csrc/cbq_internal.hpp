@@ -36,6 +36,10 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
                                   hipStream_t stream);
 
 size_t route_workspace_bytes(int64_t T, int E);
+// The library's own route scratch (no allocation): its size, and its device address on
+// the current device (looked up on that device's first call).
+size_t route_scratch_bytes();
+hipError_t route_scratch(int32_t** out);
 hipError_t launch_route(const float* logits, int64_t T, int E, int topk, int renormalize,
                         int n_shared, int32_t* ids, float* w, int32_t* offsets,
                         int32_t* sorted_tokens, int32_t* slot_of, int32_t* ws, hipStream_t stream);

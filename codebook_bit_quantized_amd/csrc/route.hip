@@ -11,6 +11,9 @@
 // Kernel 2: one workgroup does a counting sort by (expert, token).  Ranks come from
 // per-expert token bitmaps, never from the order of atomics, so every integer output
 // is deterministic.
+#include <atomic>
+#include <mutex>
+
 #include "cbq_internal.hpp"
 
 namespace cbq {
@@ -270,6 +273,44 @@ size_t route_workspace_bytes(int64_t T, int E) {
   if (T <= 0) return 0;
   const int64_t ch = route_chunk(T);
   return (size_t)((T + ch - 1) / ch) * (size_t)E * sizeof(int32_t);
+}
+
+// Scratch for callers that cannot allocate: the per-chunk expert counts of the largest
+// call (256 chunks x 256 experts), in a module-scope device array.  Every GPU that runs
+// the library holds its own copy until the process ends.  Host code never uses the
+// array's name as an address (on the host it only stands for the symbol): the device
+// address comes from hipGetSymbolAddress, looked up once per device on that device's
+// first call and kept per device.
+constexpr size_t kRouteScratchBytes = 256 * 256 * sizeof(int32_t);
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t route_scratch_bytes() { return kRouteScratchBytes; }
+
+hipError_t route_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<int32_t*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int topk, int renormalize,

@@ -188,6 +188,25 @@ int cbq_moe_route_gather(const float* logits, int64_t T, int32_t E, int32_t topk
                          int32_t* slot_of, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * cbq_moe_route_gather_noalloc - cbq_moe_route_gather without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ *  Arguments and outputs as cbq_moe_route_gather; the per-chunk expert counts go to a
+ *  scratch array of 256 KiB inside the library (one per GPU, held until the process
+ *  ends), which covers every size the routing accepts (T <= 2^24, E <= 256).  The call
+ *  allocates nothing; its first call on a device looks the array's address up once.
+ *  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ *  different streams, or from different threads) race and give undefined results;
+ *  calls ordered on one stream are safe.  The array needs no clearing (each call
+ *  rewrites the part it reads).  Outputs are bit-identical to cbq_moe_route_gather's.
+ */
+int cbq_moe_route_gather_noalloc(const float* logits, int64_t T, int32_t E, int32_t topk,
+                                 int32_t renormalize, int32_t n_shared, int32_t* topk_ids,
+                                 float* topk_w, int32_t* expert_offsets, int32_t* sorted_tokens,
+                                 int32_t* slot_of, void* stream);
+
+/*
  * cbq_codebook_lut_gemm - grouped expert GEMM with codebook weights.
  * Passage: CodeQuant2, Figure 4 (the kernel builds a table once, then reads products
  * from on-chip memory instead of multiplying) and Figure 3 (per-row centroid codebooks); the

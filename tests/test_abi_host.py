@@ -126,6 +126,12 @@ def test_route_validation():
     assert rg(P, -1, 8, 2, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL
     assert rg(None, 4, 8, 2, 1, 0, P, P, P, P, P, None, 0, None) == cbq.CBQ_EINVAL       # null logits
     assert rg(P, 4, 8, 2, 1, 0, P, P, None, P, P, None, 0, None) == cbq.CBQ_EINVAL       # null offsets
+    # the no-allocation variant validates the same way, without a workspace argument
+    rn = lib.cbq_moe_route_gather_noalloc
+    assert rn(P, 4, 300, 1, 1, 0, P, P, P, P, P, None) == cbq.CBQ_EUNSUPPORTED         # E > 256
+    assert rn(P, 4, 8, 9, 1, 0, P, P, P, P, P, None) == cbq.CBQ_EINVAL                # topk > 8
+    assert rn(P, (1 << 24) + 1, 8, 2, 1, 0, P, P, P, P, P, None) == cbq.CBQ_EUNSUPPORTED
+    assert rn(P, 4, 8, 2, 1, 0, P, P, None, P, P, None) == cbq.CBQ_EINVAL              # null offsets
 
 
 def _w(E=1, N=64, K=256, bits=4, idx=0x1000, cb=0x2000):
