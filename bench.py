@@ -211,7 +211,7 @@ class DensePhase:
             cbq.rotate_quantize(b["x"], a, codes=b["codes"], scales=b["scales"], stream=stream)
             if which == "gate_up" and self.ev is not None:
                 self.ev[0].record()
-            cbq.codebook_lut_gemm(b["codes"], b["scales"], a, [self.W[which]], path=cbq.PATH_AUTO,
+            cbq.codebook_lut_gemm(b["codes"], b["scales"], a, [self.W[which]], path=self.path_gu,
                                   out=b["out"], stream=stream)
             if which == "gate_up" and self.ev is not None:
                 self.ev[1].record()
@@ -219,7 +219,7 @@ class DensePhase:
     def gemm_gu_only(self):
         b = self.io["gate_up"]
         self.cbq.codebook_lut_gemm(b["codes"], b["scales"], self.wl.act_bits,
-                                   [self.W["gate_up"]], path=self.cbq.PATH_AUTO, out=b["out"])
+                                   [self.W["gate_up"]], path=self.path_gu, out=b["out"])
 
 
 def choose_path(cbq, counts, routed_E):
@@ -646,6 +646,78 @@ def bench_crossover(args, cbq, torch):
                           cache_flush=args.flush, results=rows)))
 
 
+def bench_decode_table(args, cbq, torch):
+    """Cold (caches flushed) rooflines of the decode GEMMs at every batch size the decode
+    workloads name: both linears of the 4B-like dense layer at T = 1 / 4 / 16 with A4 and
+    A8 activations, the gate/up GEMM of the 128-expert layer at T = 1 / 8 / 64 and of the
+    64 + 2 expert layer at T = 32, against 8 TB/s.  Each GEMM runs on the LUT path with
+    both codebook table placements where they differ (2- and 3-bit codebooks)."""
+    dev = "cuda:0"
+    flush = CacheFlush(torch, dev, args.flush)
+
+    def cold_us(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e) * 1000.0)
+        return float(np.median(ts))
+
+    def upw(ws):
+        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
+                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
+                                   K=ws.K, bits=ws.bits)
+
+    def entry(label, T, nbytes, us, **kw):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return dict(gemm=label, tokens=T, algorithmic_bytes=int(nbytes), median_us=round(us, 2),
+                    achieved_GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4), **kw)
+
+    reps = max(5, args.decode_reps)
+    rows = []
+    wl = datagen.WORKLOADS["dense2560x9728"]
+    for which, (K, N) in (("gate_up", (wl.K, wl.N)), ("down", (wl.N, wl.K))):
+        Wd = upw(datagen.dense_weights(wl, which))
+        wbytes = N * K * wl.bits // 8 + N * (1 << wl.bits) * 2
+        for a in (4, 8):
+            for T in wl.T_list:
+                xt = torch.from_numpy(datagen.dense_tokens(wl, T, which).view(np.int16)).to(dev)
+                codes, scales = cbq.rotate_quantize(xt.view(torch.bfloat16), a)
+                out = torch.empty((T, N), dtype=torch.float32, device=dev)
+                us = cold_us(lambda: cbq.codebook_lut_gemm(codes, scales, a, [Wd], path=cbq.PATH_LUT,
+                                                           out=out), reps)
+                nbytes = wbytes + T * (K * a // 8 + 4) + T * N * 4
+                rows.append(entry(f"dense {K}->{N}", T, nbytes, us, act_bits=a, bits=wl.bits))
+        del Wd
+    for name, Ts in (("moe128_h2048_f768", (1, 8, 64)), ("moe64s2_h2048_f1408", (32,))):
+        wl = datagen.WORKLOADS[name]
+        g, u, d = datagen.moe_weights(wl)
+        W = dict(gate=upw(g), up=upw(u), down=upw(d))
+        placements = (("lds", cbq.PATH_LDS_TABLES), ("reg", cbq.PATH_REG_TABLES)) \
+            if wl.bits_gate_up <= 3 else (("reg", 0),)
+        for T in Ts:
+            x, lg = datagen.moe_tokens(wl, T, decode=(name == "moe64s2_h2048_f1408"))
+            for tname, flag in placements:
+                ph = MoEPhase(cbq, torch, wl, W, x, lg, cbq.PATH_LUT | flag, cbq.PATH_LUT | flag)
+                ph.run()
+                torch.cuda.synchronize()
+                counts = np.diff(ph.rt["offsets"].cpu().numpy().astype(np.int64))
+                us = cold_us(ph.gemm_gu_only, reps)
+                rows.append(entry(f"{name} gate/up+SwiGLU", T, gate_up_bytes(wl, counts, T), us,
+                                  act_bits=wl.act_bits, bits=wl.bits_gate_up, tables=tname,
+                                  active_experts=int((counts[:wl.E] > 0).sum()) + wl.n_shared))
+        del W
+    del flush
+    print(json.dumps(dict(mode="decode_table", cache_flush=args.flush, peak_GBs=HBM_PEAK_GBS,
+                          reps=reps, results=rows)))
+
+
 def bench_dense_rotation(args, cbq, torch):
     """The dense-rotation variant of rotate_quantize on the workload's layer input
     (T prefill tokens x H channels, R a seeded H x H stand-in for a learned rotation):
@@ -716,11 +788,18 @@ def main():
                     help="measure offline codebook construction (per-row K-means) instead")
     ap.add_argument("--path", choices=("choose", "lut", "mfma"), default="choose",
                     help="GEMM path of every MoE phase: as AUTO would choose (default), or forced")
+    ap.add_argument("--tables", choices=("default", "lds", "reg"), default="default",
+                    help="where 2- and 3-bit codebooks are looked up: each path's default (LDS "
+                         "pair tables for the LUT path, register tables for the MFMA path), or "
+                         "forced for every GEMM")
     ap.add_argument("--dense-rotation", action="store_true",
                     help="measure the dense K x K rotation variant of rotate_quantize instead")
     ap.add_argument("--decode-overlap", choices=("down", "serial"), default="down",
                     help="down: the decode batch runs on a second stream, beside the prefill "
                          "batch's down projection; serial: after the prefill batch, on one stream")
+    ap.add_argument("--decode-table", action="store_true",
+                    help="cold HBM rooflines of every decode GEMM (dense T 1/4/16 with A4 and A8, "
+                         "128-expert T 1/8/64, 64 + 2 expert T 32) instead")
     ap.add_argument("--crossover", action="store_true",
                     help="time the LUT and MFMA paths against rows per expert instead")
     ap.add_argument("--peaks", action="store_true",
@@ -770,6 +849,9 @@ def main():
     if args.crossover:
         bench_crossover(args, cbq, torch)
         return
+    if args.decode_table:
+        bench_decode_table(args, cbq, torch)
+        return
     if args.dense_rotation:
         bench_dense_rotation(args, cbq, torch)
         return
@@ -782,6 +864,7 @@ def main():
                                    codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
                                    K=ws.K, bits=ws.bits)
 
+    tflag = {"default": 0, "reg": cbq.PATH_REG_TABLES, "lds": cbq.PATH_LDS_TABLES}[args.tables]
     phases = []
     if wl.kind == "moe":
         weights_np = datagen.moe_weights(wl)
@@ -797,7 +880,7 @@ def main():
             counts = np.diff(offs)
             ph.counts = counts
             ph.path_gu = ph.path_dn = (choose_path(cbq, counts, wl.E) if args.path == "choose" else
-                                       cbq.PATH_LUT if args.path == "lut" else cbq.PATH_MFMA)
+                                       cbq.PATH_LUT if args.path == "lut" else cbq.PATH_MFMA) | tflag
             ph.decode = decode or T <= 64
             phases.append(ph)
     else:
@@ -806,6 +889,7 @@ def main():
         for T in wl.T_list:
             xs = {w: datagen.dense_tokens(wl, T, w) for w in ("gate_up", "down")}
             ph = DensePhase(cbq, torch, wl, W, xs)
+            ph.path_gu = ph.path_dn = cbq.PATH_AUTO | tflag
             ph.run()
             phases.append(ph)
         torch.cuda.synchronize()
@@ -879,7 +963,7 @@ def main():
                     cache_flush=args.flush, **extra)
 
     decode_info = None
-    if wl.kind == "moe" and dom.path_gu == cbq.PATH_MFMA:
+    if wl.kind == "moe" and (dom.path_gu & 0xF) == cbq.PATH_MFMA:
         dom_flops = gate_up_flops(wl, dom.counts)
         achieved = dom_flops / (dom_ms / 1000.0) / 1e12
         roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=F16_MFMA_PEAK_TFLOPS,
@@ -918,6 +1002,7 @@ def main():
         cfg = dict(workload=wl.name, tokens_per_step=tokens, phases=[p.T for p in phases],
                    linears=[f"{wl.K}->{wl.N}", f"{wl.N}->{wl.K}"], bits=wl.bits,
                    act_bits=wl.act_bits, paths={str(p.T): int(p.path_gu) for p in phases})
+    cfg["tables"] = args.tables
     line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,

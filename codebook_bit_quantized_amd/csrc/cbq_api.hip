@@ -207,6 +207,10 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   } else {
     return fail(CBQ_EINVAL, "unknown epilogue %d", epilogue);
   }
+  const int tflags = path & (CBQ_PATH_REG_TABLES | CBQ_PATH_LDS_TABLES);
+  if (tflags == (CBQ_PATH_REG_TABLES | CBQ_PATH_LDS_TABLES))
+    return fail(CBQ_EINVAL, "CBQ_PATH_REG_TABLES and CBQ_PATH_LDS_TABLES exclude each other");
+  path &= ~(CBQ_PATH_REG_TABLES | CBQ_PATH_LDS_TABLES);
   if (path < CBQ_PATH_AUTO || path > CBQ_PATH_MFMA) return fail(CBQ_EINVAL, "unknown path %d", path);
   if (n_rows < 0) return fail(CBQ_EINVAL, "n_rows must be >= 0");
   if (n_rows > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "n_rows must be < 2^31");
@@ -231,6 +235,8 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   a.w[1] = n_w == 2 ? cbq::GemmW{W[1].idx, W[1].codebook} : a.w[0];
   a.n_w = n_w; a.E = W[0].E; a.N = W[0].N; a.K = W[0].K; a.bits = W[0].bits;
   a.swiglu = epilogue == CBQ_EPI_SWIGLU_BF16;
+  a.tables = tflags == CBQ_PATH_REG_TABLES ? cbq::kTablesReg
+             : tflags == CBQ_PATH_LDS_TABLES ? cbq::kTablesLds : cbq::kTablesDefault;
   a.out = out; a.ldo = ldo;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;

@@ -173,6 +173,114 @@ __device__ __forceinline__ void codes32_to_f16(const uint32_t* c, uint32_t* d) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Natural pair order.  The LDS pair tables below give each weight pair in index order,
+// (k0, k1) (k2, k3) (k4, k5) (k6, k7) per group of eight, so a GEMM that reads them takes
+// its activation fragments from these converters instead.
+// A4: for byte j the permute gives (b, 0x64, b, 0x64); masking to (0x640L, 0x64H0) makes
+// the low half fp16 1024 + L and the high half 1024 + 16 H; one packed fma scales the high
+// half by 1/16 and removes both offsets (each step exact in fp16).
+__device__ __forceinline__ void codes4_to_f16_nat(uint32_t x, uint32_t* d) {
+  const uint32_t xb = x ^ 0x88888888u;          // nibble v -> v + 8
+  const f16x2 mul = {(_Float16)1.0f, (_Float16)0.0625f};
+  const f16x2 add = {(_Float16)-1032.0f, (_Float16)-72.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = perm(0x64646464u, xb, 0x04000400u + 0x00010001u * (uint32_t)j) & 0xFFF0FF0Fu;
+    d[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, t), mul, add));
+  }
+}
+
+// A8, natural order: (k0, k1) (k2, k3) from x0, (k4, k5) (k6, k7) from x1.
+__device__ __forceinline__ void codes8_to_f16_nat(uint32_t x0, uint32_t x1, uint32_t* d) {
+  const uint32_t b0 = x0 ^ 0x80808080u, b1 = x1 ^ 0x80808080u;   // c -> c + 128
+  d[0] = pk_add_f16(perm(0x64646464u, b0, 0x04010400u), -1152.0f);
+  d[1] = pk_add_f16(perm(0x64646464u, b0, 0x04030402u), -1152.0f);
+  d[2] = pk_add_f16(perm(0x64646464u, b1, 0x04010400u), -1152.0f);
+  d[3] = pk_add_f16(perm(0x64646464u, b1, 0x04030402u), -1152.0f);
+}
+
+// Eight codes (group p of 32: one dword for A4, two for A8) -> four dwords, in the pair
+// order NAT (natural) or the grouped order of the register dequantisers.
+template <int ABITS, bool NAT>
+__device__ __forceinline__ void codes8_group(const uint32_t* c, int p, uint32_t* d) {
+  if constexpr (ABITS == 4) {
+    if constexpr (NAT) codes4_to_f16_nat(c[p], d);
+    else codes4_to_f16(c[p], d);
+  } else {
+    if constexpr (NAT) codes8_to_f16_nat(c[2 * p], c[2 * p + 1], d);
+    else codes8_to_f16(c[2 * p], c[2 * p + 1], d);
+  }
+}
+
+template <int ABITS, bool NAT>
+__device__ __forceinline__ void codes32_to_f16_ord(const uint32_t* c, uint32_t* d) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) codes8_group<ABITS, NAT>(c, p, d + 4 * p);
+}
+
+// ---------------------------------------------------------------------------
+// LDS pair tables for 2- and 3-bit codebooks (CodeQuant2, Figure 4: the kernel's table
+// sits in on-chip shared memory).  Two consecutive indices 2j, 2j+1 of a row form the
+// 2*BITS-bit field v = i_2j | i_2j+1 << BITS of its bitstream; entry v of the row's table
+// is the dword C[v & (L-1)] | C[v >> BITS] << 16, both weights as an fp16 pair in index
+// order.  A lookup is one field extract, one address add and one ds_read_b32 per two
+// weights, against about five vector instructions for the register tables.  The tables
+// of R rows are interleaved (entry v of row r at dword v*R + r), so lanes that read
+// different rows read different banks.
+template <int BITS>
+struct PairTab {
+  static constexpr int L = 1 << BITS;
+  static constexpr int NE = L * L;   // entries per row
+};
+
+// Field j (0..15) of the 32 indices a lane holds in w[0..BITS-1] (LSB-first).
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_field(const uint32_t* w, int j) {
+  constexpr int FB = 2 * BITS;
+  const int off = j * FB, wi = off >> 5, sh = off & 31;
+  if (sh + FB <= 32) return __builtin_amdgcn_ubfe(w[wi], (uint32_t)sh, (uint32_t)FB);
+  return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], (uint32_t)sh) & ((1u << FB) - 1u);
+}
+
+// Pairs 4p .. 4p+3 of the lane's 32 indices -> d[0..3], from the table row whose entry 0
+// is dword `row` of `tab` (entries R dwords apart).
+template <int BITS, int R>
+__device__ __forceinline__ void pair_lookup8(const uint32_t* tab, uint32_t row, const uint32_t* w,
+                                             int p, uint32_t* d) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = tab[row + pair_field<BITS>(w, 4 * p + q) * R];
+}
+
+template <int BITS, int R>
+__device__ __forceinline__ void pair_lookup32(const uint32_t* tab, uint32_t row, const uint32_t* w,
+                                              uint32_t* d) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pair_lookup8<BITS, R>(tab, row, w, p, d + 4 * p);
+}
+
+// This lane's share of one row's table: P lanes (sub = 0 .. P-1) build the row, lane sub
+// the entries whose high index is sub*H .. sub*H + H - 1 (H = L / P), from the row's
+// codebook cb (L fp16 in L/2 dwords).  Entry rows are R dwords apart from `row` on.
+template <int BITS, int P, int R>
+__device__ __forceinline__ void pair_build(uint32_t* tab, uint32_t row, const uint32_t* cb, int sub) {
+  constexpr int L = 1 << BITS;
+  constexpr int H = L / P;
+  static_assert(H >= 1 && H * P == L, "P must divide L");
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const int q = sub * H + h;                 // high index: C[q] in the upper half
+    uint32_t cw = cb[0];
+#pragma unroll
+    for (int k = 1; k < L / 2; ++k) cw = (q >> 1) == k ? cb[k] : cw;
+    const uint32_t hv = (q & 1) ? (cw >> 16) : cw;
+    uint32_t* dst = tab + row + (uint32_t)(q * L) * R;
+#pragma unroll
+    for (int lo = 0; lo < L; ++lo)
+      dst[lo * R] = perm(hv, cb[lo >> 1], (lo & 1) ? 0x05040302u : 0x05040100u);
+  }
+}
+
 // Buffer-resource loads.  A load whose byte offset is at or past num_records returns
 // zeros without faulting, so a disabled load is just an out-of-range offset and no
 // select has to touch the loaded registers (which would force an early wait).

@@ -9,6 +9,10 @@
 
 namespace cbq {
 
+// Where 2- and 3-bit codebooks are looked up: each path's default, register tables or
+// LDS pair tables.
+enum { kTablesDefault = 0, kTablesReg = 1, kTablesLds = 2 };
+
 // Device view of one weight set (see cbq_weights in cbq.h).
 struct GemmW {
   const uint8_t* idx;
@@ -26,6 +30,7 @@ struct GemmArgs {
   int n_w;
   int E, N, K, bits;
   bool swiglu;
+  int tables;               // kTables*: placement of 2- and 3-bit codebook tables
   void* out;
   int64_t ldo;
 };

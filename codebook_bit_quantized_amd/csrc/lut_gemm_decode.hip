@@ -50,13 +50,19 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t* 
   }
 }
 
-template <int BITS, int ABITS, int NW, int MSUB, int NG>
+// LT: weights looked up in LDS pair tables (2- and 3-bit codebooks), shared by the
+// workgroup's waves (they serve the same rows); otherwise in per-row register tables.
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT>
 __global__ void __launch_bounds__(NW == 2 ? 512 : 1024, BITS <= 3 ? 4 : 3)
 lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                   GemmW w0, GemmW w1, int64_t n_rows, int N, int K, int splitk, int max_rows,
                   void* __restrict__ out, int64_t ldo) {
-  extern __shared__ f32x4 red[];   // [(splitk-1) * NG * NW * MSUB][64]
+  // [(splitk-1) * NG * NW * MSUB][64] f32x4 of split-K partial sums, then (LT) the pair
+  // tables: [NG * NW][NE entries][16 rows] dwords
+  extern __shared__ f32x4 red[];
+  constexpr int NE = LT ? PairTab<BITS>::NE : 1;
+  uint32_t* const ptab = reinterpret_cast<uint32_t*>(red + (size_t)(splitk - 1) * NG * NW * MSUB * 64);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Experts in reverse order: the shared experts come last in the row order and always
@@ -82,7 +88,8 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   int nrow[NG];
   bool nvalid[NG];
   uint32_t wlane[NG];
-  RowTable<BITS> tab[NG][NW];
+  RowTable<BITS> tab[NG][NW];   // register tables (unused with LT)
+  uint32_t trow[NG][NW];        // LT: dword of entry 0 of this lane's row in each table
   __amdgpu_buffer_rsrc_t wres[NW];
   wres[0] = make_rsrc(w0.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
   if constexpr (NW == 2) wres[1] = make_rsrc(w1.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
@@ -93,9 +100,28 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     nvalid[q] = n < N;
     const int nn = nvalid[q] ? n : 0;
     wlane[q] = nvalid[q] ? (uint32_t)(n * row_bytes) + (uint32_t)(g * 4 * BITS) : kOffNone;
-    tab[q][0].load(w0.codebook + ((int64_t)e * N + nn) * L);
-    if constexpr (NW == 2) tab[q][1].load(w1.codebook + ((int64_t)e * N + nn) * L);
+    if constexpr (LT) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        trow[q][w] = (uint32_t)((q * NW + w) * NE * 16 + nl);
+        // the 4 lanes of each row in one wave build its table; tables go round the waves
+        if ((q * NW + w) % splitk == wave) {
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(
+              (w == 0 ? w0.codebook : w1.codebook) + ((int64_t)e * N + nn) * L);
+          uint32_t cb[L / 2];
+#pragma unroll
+          for (int i = 0; i < L / 2; ++i) cb[i] = src[i];
+          pair_build<BITS, 4, 16>(ptab, trow[q][w], cb, g);
+        }
+      }
+    } else {
+      tab[q][0].load(w0.codebook + ((int64_t)e * N + nn) * L);
+      if constexpr (NW == 2) tab[q][1].load(w1.codebook + ((int64_t)e * N + nn) * L);
+    }
   }
+  // tables built by other waves of the workgroup must be complete before any lookup
+  // (a wave's own LDS writes precede its reads in order, so one wave needs no barrier)
+  if (LT && splitk > 1) lds_barrier();
   const __amdgpu_buffer_rsrc_t cres = make_rsrc(codes, 0x7FFFFFFFu);
 
   const int nchunks = (K + 127) >> 7;
@@ -154,12 +180,15 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
         // one row group: convert each token sub-tile just before its MFMAs
         uint32_t bd[NW][16];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[0][w], cur.w[0][w], bd[w]);
+        for (int w = 0; w < NW; ++w) {
+          if constexpr (LT) pair_lookup32<BITS, 16>(ptab, trow[0][w], cur.w[0][w], bd[w]);
+          else dequant32<BITS>(tab[0][w], cur.w[0][w], bd[w]);
+        }
 #pragma unroll
         for (int s = 0; s < MSUB; ++s) {
           if (s >= nsub) break;
           uint32_t ad[16];
-          codes32_to_f16<ABITS>(cur.a[s], ad);
+          codes32_to_f16_ord<ABITS, LT>(cur.a[s], ad);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const f16x8 A = as_f16x8(ad[4 * j], ad[4 * j + 1], ad[4 * j + 2], ad[4 * j + 3]);
@@ -175,12 +204,15 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
       uint32_t ad[MSUB][16];
 #pragma unroll
       for (int s = 0; s < MSUB; ++s)
-        if (s < nsub) codes32_to_f16<ABITS>(cur.a[s], ad[s]);
+        if (s < nsub) codes32_to_f16_ord<ABITS, LT>(cur.a[s], ad[s]);
 #pragma unroll
       for (int q = 0; q < NG; ++q) {
         uint32_t bd[NW][16];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) dequant32<BITS>(tab[q][w], cur.w[q][w], bd[w]);
+        for (int w = 0; w < NW; ++w) {
+          if constexpr (LT) pair_lookup32<BITS, 16>(ptab, trow[q][w], cur.w[q][w], bd[w]);
+          else dequant32<BITS>(tab[q][w], cur.w[q][w], bd[w]);
+        }
 #pragma unroll
         for (int s = 0; s < MSUB; ++s) {
           if (s >= nsub) break;
@@ -259,12 +291,13 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   }
 }
 
-template <int BITS, int ABITS, int NW, int MSUB, int NG>
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT>
 static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
   dim3 grid((unsigned)((a.N + 16 * NG - 1) / (16 * NG)), (unsigned)E);
-  const size_t lds = (size_t)(splitk - 1) * NG * NW * MSUB * 64 * sizeof(f32x4);
-  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG>), grid, dim3(64 * splitk), lds,
+  const size_t lds = (size_t)(splitk - 1) * NG * NW * MSUB * 64 * sizeof(f32x4) +
+                     (LT ? (size_t)NG * NW * PairTab<BITS>::NE * 16 * sizeof(uint32_t) : 0);
+  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG, LT>), grid, dim3(64 * splitk), lds,
                      stream, a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows,
                      a.N, a.K, splitk, max_rows, a.out, a.ldo);
   return hipGetLastError();
@@ -275,11 +308,22 @@ static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStrea
 // tables (32 VGPRs per row) keep one, as more registers would cost occupancy.
 static int decode_groups(int bits, int n_w) { return (n_w == 1 && bits <= 3) ? 2 : 1; }
 
+template <int BITS, int ABITS, bool LT>
+static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStream_t s) {
+  if (a.n_w == 2) return launch_t<BITS, ABITS, 2, 2, 1, LT>(a, max_rows, splitk, s);
+  if constexpr (BITS <= 3) return launch_t<BITS, ABITS, 1, 2, 2, LT>(a, max_rows, splitk, s);
+  else return launch_t<BITS, ABITS, 1, 2, 1, LT>(a, max_rows, splitk, s);
+}
+
+// 2- and 3-bit codebooks: LDS pair tables unless the register tables are asked for (the
+// lookups take fewer vector instructions, and the LDS tables measured slightly faster
+// here); 4-bit pair tables would take 256 entries a row, so 4-bit tables stay in registers
 template <int BITS, int ABITS>
 static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStream_t s) {
-  if (a.n_w == 2) return launch_t<BITS, ABITS, 2, 2, 1>(a, max_rows, splitk, s);
-  if constexpr (BITS <= 3) return launch_t<BITS, ABITS, 1, 2, 2>(a, max_rows, splitk, s);
-  else return launch_t<BITS, ABITS, 1, 2, 1>(a, max_rows, splitk, s);
+  if constexpr (BITS <= 3) {
+    if (a.tables != kTablesReg) return launch_b<BITS, ABITS, true>(a, max_rows, splitk, s);
+  }
+  return launch_b<BITS, ABITS, false>(a, max_rows, splitk, s);
 }
 
 hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream) {

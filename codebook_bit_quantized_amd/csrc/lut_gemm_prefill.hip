@@ -32,8 +32,10 @@ constexpr int MSUB = BM / 32;
 
 }  // namespace
 
-// Everything a tile needs after scheduling; shared by the per-NMS K-loops.
-template <int BITS, int ABITS>
+// Everything a tile needs after scheduling; shared by the per-NMS K-loops.  LT: the
+// weights are looked up in LDS pair tables (2- and 3-bit codebooks); otherwise in the
+// per-row register tables.
+template <int BITS, int ABITS, bool LT>
 struct TileCtx {
   __amdgpu_buffer_rsrc_t wres[2];   // this expert's index block of each matrix
   __amdgpu_buffer_rsrc_t cres;      // the activation codes
@@ -41,13 +43,15 @@ struct TileCtx {
   uint32_t crow_off;                // byte offset of this thread's activation row
   bool nvalid[2];
   int nrow[2];
-  RowTable<BITS> tab[2];
+  RowTable<BITS> tab[2];            // register tables (unused with LT)
+  const uint32_t* ptab;             // LDS pair tables (LT)
+  uint32_t trow[2];                 // dword of entry 0 of this lane's row in each table
   bool avalid;
   int K, g, nl, tid, rows;
 };
 
-template <int BITS, int ABITS, int NW, int NMS>
-__device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t (*As)[BM * LDW],
+template <int BITS, int ABITS, int NW, int NMS, bool LT>
+__device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint16_t (*As)[BM * LDW],
                                          const float* s_scale, const uint32_t* s_rowoff,
                                          __amdgpu_buffer_rsrc_t ores) {
   const int K = c.K, g = c.g, nl = c.nl, tid = c.tid;
@@ -88,7 +92,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
     u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][tid * LDW]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      codes32_to_f16<ABITS>(a + h * ABITS, d);
+      codes32_to_f16_ord<ABITS, LT>(a + h * ABITS, d);
 #pragma unroll
       for (int j = 0; j < 4; ++j) ap[h * 4 + j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
     }
@@ -102,9 +106,12 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   // (with the activation conversion and the first matrix's dequantisation); sub-step
   // 3 runs after it from fragments already in registers, so the next step's first
   // fragment reads (which need the barrier) overlap MFMAs instead of stalling.
-  // Piece j (0..3) of one lane's 32-index dequantisation: indices 8j..8j+7.
-  auto dq_piece = [&](const RowTable<BITS>& t, const uint32_t (&w)[BITS], uint32_t* d, int j) {
-    if constexpr (BITS == 4) {
+  // Piece j (0..3) of one lane's 32-index dequantisation of matrix slot s: indices 8j..8j+7.
+  auto dq_piece = [&](int s, const uint32_t (&w)[BITS], uint32_t* d, int j) {
+    const RowTable<BITS>& t = c.tab[s];
+    if constexpr (LT) {
+      pair_lookup8<BITS, 32>(c.ptab, c.trow[s], w, j, d + 4 * j);
+    } else if constexpr (BITS == 4) {
       dequant4(t, w[j], d + 4 * j);
     } else if constexpr (BITS == 3) {
       const uint32_t f = j == 0 ? w[0] : j == 1 ? __builtin_amdgcn_alignbit(w[1], w[0], 24)
@@ -121,8 +128,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   auto a_piece = [&](int buf, const uint32_t* a, int p) {
     uint32_t d[4];
     const int h = p >> 2, j = p & 3;
-    if constexpr (ABITS == 4) codes4_to_f16(a[h * 4 + j], d);
-    else codes8_to_f16(a[h * 8 + 2 * j], a[h * 8 + 2 * j + 1], d);
+    codes8_group<ABITS, LT>(a + h * ABITS, j, d);
     u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][tid * LDW]);
     ap[p] = u32x4{d[0], d[1], d[2], d[3]};
   };
@@ -149,7 +155,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
 #pragma unroll
         for (int p = (12 * i + PRE - 1) / PRE; p < (12 * (i + 1) + PRE - 1) / PRE; ++p) {
           if (p < 8) a_piece(buf ^ 1, an, p);
-          else dq_piece(c.tab[0], wn[0], bn[0], p - 8);
+          else dq_piece(0, wn[0], bn[0], p - 8);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -165,7 +171,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
         af[ms] = frag(buf ^ 1, 0, ms);
 #pragma unroll
         for (int p = (4 * ms + NMS - 1) / NMS; p < (4 * (ms + 1) + NMS - 1) / NMS; ++p)
-          dq_piece(c.tab[1], wn[1], bn[1], p);
+          dq_piece(1, wn[1], bn[1], p);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -175,7 +181,10 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   gload(1, rw[1], ra[1]);
   astore(0, ra[0]);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) dequant32<BITS>(c.tab[s], rw[0][s], bdA[s]);
+  for (int s = 0; s < 2; ++s) {
+    if constexpr (LT) pair_lookup32<BITS, 32>(c.ptab, c.trow[s], rw[0][s], bdA[s]);
+    else dequant32<BITS>(c.tab[s], rw[0][s], bdA[s]);
+  }
   lds_barrier();
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms) af[ms] = frag(0, 0, ms);
@@ -232,12 +241,15 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS>& c, uint16_t
   }
 }
 
-template <int BITS, int ABITS, int NW>
+template <int BITS, int ABITS, int NW, bool LT>
 __global__ void __launch_bounds__(256, 1)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
                     void* __restrict__ out, int64_t ldo) {
+  // LDS pair tables: per wave, two matrix slots of 32 rows, NE entries each
+  constexpr int NE = LT ? PairTab<BITS>::NE : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t Tab[LT ? 4 * 2 * NE * 32 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDW];
   __shared__ __attribute__((aligned(16))) float s_scale[BM];
   __shared__ __attribute__((aligned(16))) uint32_t s_rowoff[BM];   // byte offset of each row in out
@@ -295,7 +307,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const int rows = (int)((me - m0) < BM ? (me - m0) : BM);
   const int nms = (rows + 31) >> 5;                  // 32-row sub-tiles holding rows
 
-  TileCtx<BITS, ABITS> c;
+  TileCtx<BITS, ABITS, LT> c;
   c.K = K;
   c.tid = tid;
   c.rows = rows;
@@ -324,12 +336,24 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   else { c.nrow[0] = n0 + wave * 64 + c.nl; c.nrow[1] = c.nrow[0] + 32; }
   constexpr int L = 1 << BITS;
   const int64_t row_bytes = (int64_t)K * BITS / 8;
+  c.ptab = Tab;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const GemmW& W = (NW == 2 && s == 1) ? w1 : w0;
     c.nvalid[s] = c.nrow[s] < N;
     const int64_t rowi = (int64_t)e * N + (c.nvalid[s] ? c.nrow[s] : 0);
-    c.tab[s].load(W.codebook + rowi * L);
+    if constexpr (LT) {
+      // this wave's tables only hold its own rows: built and read by the wave itself,
+      // so no barrier is needed (a wave's LDS accesses complete in order)
+      uint32_t cb[L / 2];
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(W.codebook + rowi * L);
+#pragma unroll
+      for (int i = 0; i < L / 2; ++i) cb[i] = src[i];
+      c.trow[s] = (uint32_t)((wave * 2 + s) * NE * 32 + c.nl);
+      pair_build<BITS, 2, 32>(Tab, c.trow[s], cb, c.g);
+    } else {
+      c.tab[s].load(W.codebook + rowi * L);
+    }
     c.wres[s] = make_rsrc(W.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
     c.wrow_off[s] = (uint32_t)((c.nvalid[s] ? c.nrow[s] : 0) * row_bytes);
   }
@@ -337,18 +361,18 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // output buffer: every row of this call (n_rows) x ldo elements
   const __amdgpu_buffer_rsrc_t ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
   switch (nms) {
-    case 1: tile_run<BITS, ABITS, NW, 1>(c, As, s_scale, s_rowoff, ores); break;
-    case 2: tile_run<BITS, ABITS, NW, 2>(c, As, s_scale, s_rowoff, ores); break;
-    case 3: tile_run<BITS, ABITS, NW, 3>(c, As, s_scale, s_rowoff, ores); break;
-    case 4: tile_run<BITS, ABITS, NW, 4>(c, As, s_scale, s_rowoff, ores); break;
-    case 5: tile_run<BITS, ABITS, NW, 5>(c, As, s_scale, s_rowoff, ores); break;
-    case 6: tile_run<BITS, ABITS, NW, 6>(c, As, s_scale, s_rowoff, ores); break;
-    case 7: tile_run<BITS, ABITS, NW, 7>(c, As, s_scale, s_rowoff, ores); break;
-    default: tile_run<BITS, ABITS, NW, 8>(c, As, s_scale, s_rowoff, ores); break;
+    case 1: tile_run<BITS, ABITS, NW, 1, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 2: tile_run<BITS, ABITS, NW, 2, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 3: tile_run<BITS, ABITS, NW, 3, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 4: tile_run<BITS, ABITS, NW, 4, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 5: tile_run<BITS, ABITS, NW, 5, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 6: tile_run<BITS, ABITS, NW, 6, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 7: tile_run<BITS, ABITS, NW, 7, LT>(c, As, s_scale, s_rowoff, ores); break;
+    default: tile_run<BITS, ABITS, NW, 8, LT>(c, As, s_scale, s_rowoff, ores); break;
   }
 }
 
-template <int BITS, int ABITS>
+template <int BITS, int ABITS, bool LT>
 static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
   const int ncol = a.n_w == 2 ? 128 : 256;
@@ -356,24 +380,28 @@ static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) 
   mtiles = (mtiles + 15) / 16 * 16;                  // a multiple of 16 (XCD pairs)
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2>), grid, dim3(256), 0, stream, a.codes,
+    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT>), grid, dim3(256), 0, stream, a.codes,
                        a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
                        min_rows, a.out, a.ldo);
   else
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1>), grid, dim3(256), 0, stream, a.codes,
+    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT>), grid, dim3(256), 0, stream, a.codes,
                        a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
                        min_rows, a.out, a.ldo);
   return hipGetLastError();
 }
 
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream) {
+  // 2- and 3-bit codebooks: register tables unless the LDS pair tables are asked for (the
+  // pair tables take fewer vector instructions but add LDS traffic to the activation
+  // tiles' reads, and measured slightly slower here); 4-bit tables stay in registers
+  const bool lt = a.tables == kTablesLds;
   switch (a.bits * 10 + (a.act_bits == 8 ? 8 : 4)) {
-    case 44: return launch_p<4, 4>(a, min_rows, stream);
-    case 48: return launch_p<4, 8>(a, min_rows, stream);
-    case 34: return launch_p<3, 4>(a, min_rows, stream);
-    case 38: return launch_p<3, 8>(a, min_rows, stream);
-    case 24: return launch_p<2, 4>(a, min_rows, stream);
-    case 28: return launch_p<2, 8>(a, min_rows, stream);
+    case 44: return launch_p<4, 4, false>(a, min_rows, stream);
+    case 48: return launch_p<4, 8, false>(a, min_rows, stream);
+    case 34: return lt ? launch_p<3, 4, true>(a, min_rows, stream) : launch_p<3, 4, false>(a, min_rows, stream);
+    case 38: return lt ? launch_p<3, 8, true>(a, min_rows, stream) : launch_p<3, 8, false>(a, min_rows, stream);
+    case 24: return lt ? launch_p<2, 4, true>(a, min_rows, stream) : launch_p<2, 4, false>(a, min_rows, stream);
+    case 28: return lt ? launch_p<2, 8, true>(a, min_rows, stream) : launch_p<2, 8, false>(a, min_rows, stream);
   }
   return hipErrorInvalidValue;
 }

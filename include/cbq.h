@@ -59,6 +59,14 @@ enum {
                          once per tile step in LDS */
 };
 
+/* Flags added to a path to choose where 2- and 3-bit codebooks are looked up (4-bit ones
+   always use the register tables).  By default the LUT path uses LDS pair tables (two
+   weights per lookup, the table the pages' kernel keeps in shared memory) and the MFMA
+   path per-row register tables (byte permutes), the faster placement of each as measured.
+   Results agree within fp32 summation order; kept to compare the two placements. */
+#define CBQ_PATH_REG_TABLES 0x10
+#define CBQ_PATH_LDS_TABLES 0x20
+
 #define CBQ_AUTO_MAX_LUT_ROWS 32
 
 /*

@@ -161,6 +161,9 @@ def test_gemm_validation():
     assert _gemm(lib, [_w(), _w(N=128)], n_w=2, epi=1) == E       # mismatched gate/up
     assert _gemm(lib, [_w()], epi=7) == E
     assert _gemm(lib, [_w()], path=3) == E
+    assert _gemm(lib, [_w()], path=cbq.PATH_LUT | 0x40) == E     # unknown flag
+    assert _gemm(lib, [_w()], path=cbq.PATH_LUT | cbq.PATH_REG_TABLES | cbq.PATH_LDS_TABLES) == E
+    assert _gemm(lib, [_w()], path=cbq.PATH_MFMA | cbq.PATH_LDS_TABLES, n_rows=0) == cbq.CBQ_OK
     assert _gemm(lib, [_w()], ldo=32) == E                        # ldo < N
     assert _gemm(lib, [_w()], ldo=66) == E                        # ldo % 4
     assert _gemm(lib, [_w()], n_rows=-1) == E

@@ -145,6 +145,21 @@ def test_dense_gemm(bits, act_bits, path, T, N, K):
     assert_normwise(y.cpu().numpy(), ref, 1e-3, f"dense bits={bits} a={act_bits} path={path}")
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("act_bits", [4, 8])
+@pytest.mark.parametrize("path", [cbq.PATH_LUT, cbq.PATH_MFMA])
+@pytest.mark.parametrize("tables", [cbq.PATH_REG_TABLES, cbq.PATH_LDS_TABLES])
+@pytest.mark.parametrize("T,N,K", [(4, 256, 256), (40, 144, 800), (150, 208, 544)])
+def test_dense_gemm_table_placements(bits, act_bits, path, tables, T, N, K):
+    """2- and 3-bit codebooks through either table placement on either path (register
+    tables or LDS pair tables): the same products, another summation order."""
+    ws, rq, ref = _dense_case(200 * bits + act_bits + T, T, N, K, bits, act_bits)
+    W = upload_weights(ws)
+    y = cbq.codebook_lut_gemm(to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits, [W],
+                              path=path | tables)
+    assert_normwise(y.cpu().numpy(), ref, 1e-3, f"tables {tables} bits={bits} a={act_bits} path={path}")
+
+
 def test_dense_gemm_identity_codebook():
     """W = I through the kernels: y = scale * q exactly (checks operand layouts)."""
     K = N = 256
@@ -159,6 +174,26 @@ def test_dense_gemm_identity_codebook():
         assert np.array_equal(y.cpu().numpy(), expect), path
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_pair_table_identity_codebook(bits):
+    """W = I with a 2- or 3-bit codebook {0, 1, 0, ...} through the LDS pair tables: every
+    output is scale * q exactly, so each table entry, its row and the pair order of the
+    lookups line up with the activation fragments (checks layouts bit for bit)."""
+    K = N = 256
+    raw = np.eye(N, K, dtype=np.uint8)[None]
+    idx = datagen.pack_lsb_first(raw, bits)
+    cbv = np.zeros((N, 1 << bits), dtype=np.float32)
+    cbv[:, 1] = 1.0
+    ws = datagen.WeightSet(1, N, K, bits, idx, datagen.f32_to_f16_bits(cbv)[None])
+    for act_bits in (4, 8):
+        rq = oracle.rotate_quantize(datagen.random_tokens(6 + act_bits, 70, K), 0, act_bits)
+        expect = rq["q"].astype(np.float32) * rq["scale"][:, None]
+        for path in (cbq.PATH_LUT, cbq.PATH_MFMA):
+            y = cbq.codebook_lut_gemm(to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits,
+                                      [upload_weights(ws)], path=path | cbq.PATH_LDS_TABLES)
+            assert np.array_equal(y.cpu().numpy(), expect), (act_bits, path)
+
+
 def _moe_case(seed, T, E, k, S, H, F, bits, act_bits):
     wl = datagen.Workload("t", 2000 + seed, "moe", act_bits, H=H, F=F, E=E, topk=k, n_shared=S,
                           bits_gate_up=bits, bits_down=bits)
@@ -167,7 +202,9 @@ def _moe_case(seed, T, E, k, S, H, F, bits, act_bits):
     return wl, gate, up, down, x, lg
 
 
-@pytest.mark.parametrize("path", [cbq.PATH_AUTO, cbq.PATH_LUT, cbq.PATH_MFMA])
+@pytest.mark.parametrize("path", [cbq.PATH_AUTO, cbq.PATH_LUT, cbq.PATH_MFMA,
+                                  cbq.PATH_AUTO | cbq.PATH_REG_TABLES,
+                                  cbq.PATH_AUTO | cbq.PATH_LDS_TABLES])
 @pytest.mark.parametrize("bits,act_bits", [(4, 4), (3, 4), (2, 8)])
 @pytest.mark.parametrize("T,E,k,S", [(6, 8, 2, 0), (96, 8, 2, 1), (300, 4, 2, 0)])
 def test_grouped_swiglu_and_down(path, bits, act_bits, T, E, k, S):
@@ -195,7 +232,8 @@ def test_grouped_swiglu_and_down(path, bits, act_bits, T, E, k, S):
 
 
 @pytest.mark.parametrize("bits,act_bits,n_w", [(3, 4, 2), (4, 8, 2), (2, 4, 1), (3, 8, 1), (4, 4, 1)])
-@pytest.mark.parametrize("path", [cbq.PATH_AUTO, cbq.PATH_LUT])
+@pytest.mark.parametrize("path", [cbq.PATH_AUTO, cbq.PATH_LUT, cbq.PATH_LUT | cbq.PATH_REG_TABLES,
+                                  cbq.PATH_MFMA | cbq.PATH_LDS_TABLES])
 def test_many_tile_decode_gemm(bits, act_bits, n_w, path):
     # 64 experts x 2080 rows: enough 16-row tiles that no wave splits K (the decode
     # layout of the large MoE layers); K = 160 leaves a 32-channel chunk tail, N = 2080
