@@ -74,6 +74,19 @@ class CacheFlush:
             self.buf.sum()
 
 
+def upload_weights(cbq, torch, ws, layout="blocked", dev="cuda:0"):
+    """A host weight set on the device, regrouped into the blocked index layout
+    (cbq_prepack_weights) unless layout == "rows"."""
+    w = cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
+                            codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
+                            K=ws.K, bits=ws.bits)
+    if layout == "rows":
+        return w
+    blk = cbq.prepack_weights(w)
+    torch.cuda.synchronize()
+    return blk
+
+
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -413,9 +426,7 @@ def bench_latency_table(args, cbq, torch):
     out = torch.empty((R, wl.H), dtype=torch.float32, device=dev)
 
     def upw(ws):
-        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
-                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
-                                   K=ws.K, bits=ws.bits)
+        return upload_weights(cbq, torch, ws, args.layout, dev)
 
     table = {}
     for bits in choices:
@@ -618,9 +629,7 @@ def bench_crossover(args, cbq, torch):
         return round(sum(ts[1:-1]) / (len(ts) - 2), 1)
 
     def upw(ws):
-        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
-                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
-                                   K=ws.K, bits=ws.bits)
+        return upload_weights(cbq, torch, ws, args.layout, dev)
 
     E = 16
     rows = []
@@ -669,50 +678,51 @@ def bench_decode_table(args, cbq, torch):
             ts.append(s.elapsed_time(e) * 1000.0)
         return float(np.median(ts))
 
-    def upw(ws):
-        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
-                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
-                                   K=ws.K, bits=ws.bits)
-
     def entry(label, T, nbytes, us, **kw):
         gbs = nbytes / (us * 1e-6) / 1e9
         return dict(gemm=label, tokens=T, algorithmic_bytes=int(nbytes), median_us=round(us, 2),
                     achieved_GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4), **kw)
 
     reps = max(5, args.decode_reps)
+    layouts = ("blocked", "rows")
     rows = []
     wl = datagen.WORKLOADS["dense2560x9728"]
     for which, (K, N) in (("gate_up", (wl.K, wl.N)), ("down", (wl.N, wl.K))):
-        Wd = upw(datagen.dense_weights(wl, which))
+        ws = datagen.dense_weights(wl, which)
         wbytes = N * K * wl.bits // 8 + N * (1 << wl.bits) * 2
-        for a in (4, 8):
-            for T in wl.T_list:
-                xt = torch.from_numpy(datagen.dense_tokens(wl, T, which).view(np.int16)).to(dev)
-                codes, scales = cbq.rotate_quantize(xt.view(torch.bfloat16), a)
-                out = torch.empty((T, N), dtype=torch.float32, device=dev)
-                us = cold_us(lambda: cbq.codebook_lut_gemm(codes, scales, a, [Wd], path=cbq.PATH_LUT,
-                                                           out=out), reps)
-                nbytes = wbytes + T * (K * a // 8 + 4) + T * N * 4
-                rows.append(entry(f"dense {K}->{N}", T, nbytes, us, act_bits=a, bits=wl.bits))
-        del Wd
+        for layout in layouts:
+            Wd = upload_weights(cbq, torch, ws, layout, dev)
+            for a in (4, 8):
+                for T in wl.T_list:
+                    xt = torch.from_numpy(datagen.dense_tokens(wl, T, which).view(np.int16)).to(dev)
+                    codes, scales = cbq.rotate_quantize(xt.view(torch.bfloat16), a)
+                    out = torch.empty((T, N), dtype=torch.float32, device=dev)
+                    us = cold_us(lambda: cbq.codebook_lut_gemm(codes, scales, a, [Wd],
+                                                               path=cbq.PATH_LUT, out=out), reps)
+                    nbytes = wbytes + T * (K * a // 8 + 4) + T * N * 4
+                    rows.append(entry(f"dense {K}->{N}", T, nbytes, us, act_bits=a, bits=wl.bits,
+                                      layout=layout))
+            del Wd
     for name, Ts in (("moe128_h2048_f768", (1, 8, 64)), ("moe64s2_h2048_f1408", (32,))):
         wl = datagen.WORKLOADS[name]
-        g, u, d = datagen.moe_weights(wl)
-        W = dict(gate=upw(g), up=upw(u), down=upw(d))
+        host = datagen.moe_weights(wl)
         placements = (("lds", cbq.PATH_LDS_TABLES), ("reg", cbq.PATH_REG_TABLES)) \
             if wl.bits_gate_up <= 3 else (("reg", 0),)
-        for T in Ts:
-            x, lg = datagen.moe_tokens(wl, T, decode=(name == "moe64s2_h2048_f1408"))
-            for tname, flag in placements:
-                ph = MoEPhase(cbq, torch, wl, W, x, lg, cbq.PATH_LUT | flag, cbq.PATH_LUT | flag)
-                ph.run()
-                torch.cuda.synchronize()
-                counts = np.diff(ph.rt["offsets"].cpu().numpy().astype(np.int64))
-                us = cold_us(ph.gemm_gu_only, reps)
-                rows.append(entry(f"{name} gate/up+SwiGLU", T, gate_up_bytes(wl, counts, T), us,
-                                  act_bits=wl.act_bits, bits=wl.bits_gate_up, tables=tname,
-                                  active_experts=int((counts[:wl.E] > 0).sum()) + wl.n_shared))
-        del W
+        for layout in layouts:
+            W = dict(zip(("gate", "up", "down"), (upload_weights(cbq, torch, w, layout, dev) for w in host)))
+            for T in Ts:
+                x, lg = datagen.moe_tokens(wl, T, decode=(name == "moe64s2_h2048_f1408"))
+                for tname, flag in placements:
+                    ph = MoEPhase(cbq, torch, wl, W, x, lg, cbq.PATH_LUT | flag, cbq.PATH_LUT | flag)
+                    ph.run()
+                    torch.cuda.synchronize()
+                    counts = np.diff(ph.rt["offsets"].cpu().numpy().astype(np.int64))
+                    us = cold_us(ph.gemm_gu_only, reps)
+                    rows.append(entry(f"{name} gate/up+SwiGLU", T, gate_up_bytes(wl, counts, T), us,
+                                      act_bits=wl.act_bits, bits=wl.bits_gate_up, tables=tname,
+                                      layout=layout,
+                                      active_experts=int((counts[:wl.E] > 0).sum()) + wl.n_shared))
+            del W
     del flush
     print(json.dumps(dict(mode="decode_table", cache_flush=args.flush, peak_GBs=HBM_PEAK_GBS,
                           reps=reps, results=rows)))
@@ -788,6 +798,9 @@ def main():
                     help="measure offline codebook construction (per-row K-means) instead")
     ap.add_argument("--path", choices=("choose", "lut", "mfma"), default="choose",
                     help="GEMM path of every MoE phase: as AUTO would choose (default), or forced")
+    ap.add_argument("--layout", choices=("blocked", "rows"), default="blocked",
+                    help="index layout the GEMMs read: regrouped by cbq_prepack_weights "
+                         "(default) or the row bitstreams as generated")
     ap.add_argument("--tables", choices=("default", "lds", "reg"), default="default",
                     help="where 2- and 3-bit codebooks are looked up: each path's default (LDS "
                          "pair tables for the LUT path, register tables for the MFMA path), or "
@@ -860,9 +873,7 @@ def main():
     t_setup = time.perf_counter()
 
     def upw(ws):
-        return cbq.CodebookWeights(idx=torch.from_numpy(ws.idx).to(dev),
-                                   codebook=torch.from_numpy(ws.codebook.view(np.int16)).to(dev),
-                                   K=ws.K, bits=ws.bits)
+        return upload_weights(cbq, torch, ws, args.layout, dev)
 
     tflag = {"default": 0, "reg": cbq.PATH_REG_TABLES, "lds": cbq.PATH_LDS_TABLES}[args.tables]
     phases = []
@@ -1003,6 +1014,7 @@ def main():
                    linears=[f"{wl.K}->{wl.N}", f"{wl.N}->{wl.K}"], bits=wl.bits,
                    act_bits=wl.act_bits, paths={str(p.T): int(p.path_gu) for p in phases})
     cfg["tables"] = args.tables
+    cfg["index_layout"] = args.layout
     line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,

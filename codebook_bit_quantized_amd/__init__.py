@@ -16,13 +16,14 @@ from ._binding import (AUTO_MAX_LUT_ROWS, CBQ_EHIP, CBQ_EINVAL, CBQ_EUNSUPPORTED
                        CBQ_OK, EPI_F32, EPI_SWIGLU_BF16, EXPORTED, LIB_PATH, PATH_AUTO, PATH_LUT,
                        PATH_MFMA, PATH_REG_TABLES, PATH_LDS_TABLES, CbqError, CodebookWeights, cbq_weights, codebook_lut_gemm,
                        cpu_lut_gemm, kmeans_codebooks, load_library, moe_combine, moe_ffn, moe_route_gather,
-                       moe_route_gather_noalloc,
+                       moe_route_gather_noalloc, prepack_weights, LAYOUT_ROWS, LAYOUT_BLOCKED,
                        refit_codebooks,
                        rotate_dense_workspace, rotate_quantize, rotate_quantize_dense,
                        route_workspace)
 
 __all__ = [
-    "rotate_quantize", "moe_route_gather", "moe_route_gather_noalloc", "codebook_lut_gemm", "moe_combine", "moe_ffn",
+    "rotate_quantize", "moe_route_gather", "moe_route_gather_noalloc", "prepack_weights", "LAYOUT_ROWS", "LAYOUT_BLOCKED",
+    "codebook_lut_gemm", "moe_combine", "moe_ffn",
     "route_workspace", "kmeans_codebooks", "refit_codebooks", "cpu_lut_gemm", "rotate_quantize_dense",
     "rotate_dense_workspace",
     "CodebookWeights", "CbqError", "load_library", "LIB_PATH", "EXPORTED", "cbq_weights",

@@ -27,7 +27,7 @@ AUTO_MAX_LUT_ROWS = 32
 # every symbol include/cbq.h declares
 EXPORTED = ("cbq_rotate_quantize", "cbq_rotate_quantize_ex", "cbq_rotate_dense_workspace",
             "cbq_rotate_quantize_dense", "cbq_route_workspace", "cbq_moe_route_gather",
-            "cbq_moe_route_gather_noalloc",
+            "cbq_moe_route_gather_noalloc", "cbq_prepack_bytes", "cbq_prepack_weights",
             "cbq_gemm_workspace", "cbq_codebook_lut_gemm", "cbq_moe_combine",
             "cbq_kmeans_codebooks", "cbq_refit_codebooks", "cbq_cpu_lut_gemm", "cbq_status_string", "cbq_last_error",
             "cbq_version")
@@ -39,9 +39,13 @@ class CbqError(RuntimeError):
         self.status = status
 
 
+LAYOUT_ROWS, LAYOUT_BLOCKED = 0, 1
+
+
 class cbq_weights(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("codebook", ctypes.c_void_p), ("E", ctypes.c_int32),
-                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32)]
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -70,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 vp, sz, vp]),
         "cbq_moe_route_gather_noalloc": (ctypes.c_int, [vp, i64, i32, i32, i32, i32, vp, vp, vp,
                                                         vp, vp, vp]),
+        "cbq_prepack_bytes": (sz, [W]),
+        "cbq_prepack_weights": (ctypes.c_int, [W, vp, vp]),
         "cbq_gemm_workspace": (sz, [W, i32, i64, i32, i32]),
         "cbq_codebook_lut_gemm": (ctypes.c_int, [vp, vp, i32, i64, vp, vp, W, i32, i32, i32, vp,
                                                  i64, vp, sz, vp]),
@@ -114,11 +120,14 @@ def _require_gpu(*ts: Optional[torch.Tensor]):
 
 @dataclass
 class CodebookWeights:
-    """One weight matrix type for E experts: packed indices and fp16 codebooks (device)."""
-    idx: torch.Tensor        # uint8 [E][N][K*bits/8]
+    """One weight matrix type for E experts: packed indices and fp16 codebooks (device).
+    idx is [E][N][K*bits/8] in the row layout, or the blocked layout's bytes as
+    [E][N][Kp*bits/8] (Kp = K rounded up to 128) after prepack_weights."""
+    idx: torch.Tensor        # uint8 [E][N][row bytes]
     codebook: torch.Tensor   # int16/uint16/float16 [E][N][2^bits]
     K: int
     bits: int
+    layout: int = LAYOUT_ROWS
 
     @property
     def E(self) -> int:
@@ -130,7 +139,7 @@ class CodebookWeights:
 
     def c_struct(self) -> cbq_weights:
         return cbq_weights(self.idx.data_ptr(), self.codebook.data_ptr(), self.E, self.N, self.K,
-                           self.bits)
+                           self.bits, self.layout)
 
 
 # ---------------------------------------------------------------------------
@@ -250,6 +259,22 @@ def moe_route_gather_noalloc(logits: torch.Tensor, topk: int, renormalize: bool 
     return dict(ids=ids, weights=w, offsets=offs, sorted_tokens=st[:R], slot_of=so)
 
 
+def prepack_weights(w: CodebookWeights, stream=None) -> CodebookWeights:
+    """The blocked-layout copy of a row-layout weight set (cbq_prepack_weights); the
+    codebooks are shared, not copied."""
+    lib = load_library()
+    _require_gpu(w.idx, w.codebook)
+    if w.layout != LAYOUT_ROWS:
+        raise ValueError("prepack_weights takes a row-layout weight set")
+    s = w.c_struct()
+    n = int(lib.cbq_prepack_bytes(ctypes.byref(s)))
+    kp = (w.K + 127) // 128 * 128
+    dst = torch.empty((w.E, w.N, kp * w.bits // 8), dtype=torch.uint8, device=w.idx.device)
+    assert dst.numel() == n
+    _check(lib.cbq_prepack_weights(ctypes.byref(s), _ptr(dst), _stream(stream)))
+    return CodebookWeights(idx=dst, codebook=w.codebook, K=w.K, bits=w.bits, layout=LAYOUT_BLOCKED)
+
+
 def codebook_lut_gemm(codes: torch.Tensor, scales: torch.Tensor, act_bits: int,
                       weights: Sequence[CodebookWeights], n_rows: Optional[int] = None,
                       expert_offsets: Optional[torch.Tensor] = None,
@@ -340,7 +365,7 @@ def cpu_lut_gemm(codes, scales, act_bits: int, idx, codebook, K: int, bits: int,
     T, N = codes.shape[0], idx.shape[0]
     if out is None:
         out = np.empty((T, N), dtype=np.float32)
-    w = cbq_weights(idx.ctypes.data, codebook.ctypes.data, 1, N, K, bits)
+    w = cbq_weights(idx.ctypes.data, codebook.ctypes.data, 1, N, K, bits, LAYOUT_ROWS)
     _check(lib.cbq_cpu_lut_gemm(ctypes.c_void_p(codes.ctypes.data), ctypes.c_void_p(scales.ctypes.data),
                                 act_bits, T, ctypes.byref(w), ctypes.c_void_p(out.ctypes.data),
                                 out.strides[0] // 4, n_threads, 0 if avx512 else CPU_NO_AVX512))

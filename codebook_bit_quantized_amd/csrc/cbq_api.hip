@@ -36,6 +36,8 @@ int check_weights(const cbq_weights* W, int i) {
   if (W->N < 16 || W->N % 16) return fail(CBQ_EINVAL, "W[%d]: N must be a positive multiple of 16 (got %d)", i, W->N);
   if (W->K < 32 || W->K % 32) return fail(CBQ_EINVAL, "W[%d]: K must be a positive multiple of 32 (got %d)", i, W->K);
   if (W->bits < 2 || W->bits > 4) return fail(CBQ_EUNSUPPORTED, "W[%d]: bits must be 2, 3 or 4 (got %d)", i, W->bits);
+  if (W->layout != CBQ_LAYOUT_ROWS && W->layout != CBQ_LAYOUT_BLOCKED)
+    return fail(CBQ_EINVAL, "W[%d]: unknown index layout %d", i, W->layout);
   return CBQ_OK;
 }
 
@@ -178,6 +180,28 @@ CBQ_EXPORT int cbq_moe_route_gather_noalloc(const float* logits, int64_t T, int3
   return CBQ_OK;
 }
 
+CBQ_EXPORT size_t cbq_prepack_bytes(const cbq_weights* src) {
+  if (!src || src->E < 1 || src->N < 16 || src->N % 16 || src->K < 32 || src->K % 32 ||
+      src->bits < 2 || src->bits > 4)
+    return 0;
+  return (size_t)src->E * src->N * cbq::index_row_bytes(src->K, src->bits, true);
+}
+
+CBQ_EXPORT int cbq_prepack_weights(const cbq_weights* src, uint8_t* dst, void* stream) {
+  g_err[0] = 0;
+  if (!src) return fail(CBQ_EINVAL, "src must be non-null");
+  if (int rc = check_weights(src, 0)) return rc;
+  if (src->layout != CBQ_LAYOUT_ROWS) return fail(CBQ_EINVAL, "src must be in the row layout");
+  if (!dst || !aligned16(dst)) return fail(CBQ_EINVAL, "dst must be non-null and 16-byte aligned");
+  const size_t n_src = (size_t)src->E * src->N * ((size_t)src->K * src->bits / 8);
+  const size_t n_dst = cbq_prepack_bytes(src);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src->idx), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (d0 < s0 + n_src && s0 < d0 + n_dst) return fail(CBQ_EINVAL, "dst must not overlap src->idx");
+  hipError_t e = cbq::launch_prepack(src->idx, dst, src->E, src->N, src->K, src->bits, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prepack_weights launch");
+  return CBQ_OK;
+}
+
 CBQ_EXPORT size_t cbq_gemm_workspace(const cbq_weights* W, int32_t n_w, int64_t n_rows,
                                      int32_t act_bits, int32_t path) {
   (void)W; (void)n_w; (void)n_rows; (void)act_bits; (void)path;
@@ -197,8 +221,9 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
     int st = check_weights(&W[i], i);
     if (st != CBQ_OK) return st;
   }
-  if (n_w == 2 && (W[1].E != W[0].E || W[1].N != W[0].N || W[1].K != W[0].K || W[1].bits != W[0].bits))
-    return fail(CBQ_EINVAL, "gate and up weights must have equal E, N, K and bits");
+  if (n_w == 2 && (W[1].E != W[0].E || W[1].N != W[0].N || W[1].K != W[0].K || W[1].bits != W[0].bits ||
+                   W[1].layout != W[0].layout))
+    return fail(CBQ_EINVAL, "gate and up weights must have equal E, N, K, bits and layout");
   if (act_bits != 4 && act_bits != 8) return fail(CBQ_EINVAL, "act_bits must be 4 or 8 (got %d)", act_bits);
   if (epilogue == CBQ_EPI_F32) {
     if (n_w != 1) return fail(CBQ_EINVAL, "CBQ_EPI_F32 takes exactly one weight set");
@@ -220,7 +245,8 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
     const int64_t esz = epilogue == CBQ_EPI_SWIGLU_BF16 ? 2 : 4;
     if (n_rows * ldo * esz >= (int64_t(1) << 30))
       return fail(CBQ_EUNSUPPORTED, "output must be smaller than 1 GiB per call (n_rows * ldo * %lld bytes)", (long long)esz);
-    if ((int64_t)W[0].N * W[0].K * W[0].bits / 8 >= (int64_t(1) << 31))
+    if ((int64_t)W[0].N * cbq::index_row_bytes(W[0].K, W[0].bits, W[0].layout == CBQ_LAYOUT_BLOCKED) >=
+        (int64_t(1) << 31))
       return fail(CBQ_EUNSUPPORTED, "one expert's index block must be smaller than 2 GiB");
     if (!row_token && n_rows * ((int64_t)W[0].K * act_bits / 8) >= (int64_t(1) << 31))
       return fail(CBQ_EUNSUPPORTED, "codes must be smaller than 2 GiB");
@@ -235,6 +261,7 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   a.w[1] = n_w == 2 ? cbq::GemmW{W[1].idx, W[1].codebook} : a.w[0];
   a.n_w = n_w; a.E = W[0].E; a.N = W[0].N; a.K = W[0].K; a.bits = W[0].bits;
   a.swiglu = epilogue == CBQ_EPI_SWIGLU_BF16;
+  a.blocked = W[0].layout == CBQ_LAYOUT_BLOCKED;
   a.tables = tflags == CBQ_PATH_REG_TABLES ? cbq::kTablesReg
              : tflags == CBQ_PATH_LDS_TABLES ? cbq::kTablesLds : cbq::kTablesDefault;
   a.out = out; a.ldo = ldo;
@@ -303,6 +330,7 @@ CBQ_EXPORT int cbq_cpu_lut_gemm(const uint8_t* codes, const float* scales, int32
   if (!W) return fail(CBQ_EINVAL, "W must be non-null");
   if (int rc = check_weights(W, 0)) return rc;
   if (W->E != 1) return fail(CBQ_EUNSUPPORTED, "the CPU kernel takes one weight set (E = 1, got %d)", W->E);
+  if (W->layout != CBQ_LAYOUT_ROWS) return fail(CBQ_EUNSUPPORTED, "the CPU kernel reads the row layout only");
   if (act_bits != 4 && act_bits != 8) return fail(CBQ_EINVAL, "act_bits must be 4 or 8 (got %d)", act_bits);
   if (T < 0) return fail(CBQ_EINVAL, "T must be >= 0");
   if (ldo < W->N) return fail(CBQ_EINVAL, "ldo must be >= N");

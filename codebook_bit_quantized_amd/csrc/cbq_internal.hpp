@@ -31,6 +31,7 @@ struct GemmArgs {
   int E, N, K, bits;
   bool swiglu;
   int tables;               // kTables*: placement of 2- and 3-bit codebook tables
+  int blocked;              // 1: indices in the blocked layout (cbq_prepack_weights)
   void* out;
   int64_t ldo;
 };
@@ -54,6 +55,17 @@ hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream
 
 // MFMA (prefill) path.  Experts with at most min_rows rows are skipped (AUTO split).
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream);
+
+// Regroups a row-layout index block [E][N][K*bits/8] into the blocked layout.
+hipError_t launch_prepack(const uint8_t* src, uint8_t* dst, int E, int N, int K, int bits,
+                          hipStream_t stream);
+
+// Bytes per row of one expert's index block: K (rows layout) or K rounded up to a
+// multiple of 128 (blocked layout), times bits / 8.
+__host__ __device__ inline int64_t index_row_bytes(int K, int bits, bool blocked) {
+  const int64_t kp = blocked ? (int64_t)(K + 127) / 128 * 128 : K;
+  return kp * bits / 8;
+}
 
 hipError_t launch_kmeans(const uint16_t* w, int64_t R, int K, int64_t ldw, int bits, int max_iters,
                          uint8_t* idx, uint16_t* codebook, int32_t* iters_done,

@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(NW == 2 ? 512 : 1024, BITS <= 3 ? 4 : 3)
 lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                   GemmW w0, GemmW w1, int64_t n_rows, int N, int K, int splitk, int max_rows,
-                  void* __restrict__ out, int64_t ldo) {
+                  int blocked, void* __restrict__ out, int64_t ldo) {
   // [(splitk-1) * NG * NW * MSUB][64] f32x4 of split-K partial sums, then (LT) the pair
   // tables: [NG * NW][NE entries][16 rows] dwords
   extern __shared__ f32x4 red[];
@@ -81,7 +81,10 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
 
   const int nl = lane & 15, g = lane >> 4;
   constexpr int L = 1 << BITS;
-  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  // bytes per row of the expert's index block; the rows layout keeps each row's bitstream,
+  // the blocked one each 16-row x 128-channel tile in 256*BITS contiguous bytes
+  const int64_t row_bytes = index_row_bytes(K, BITS, blocked != 0);
+  const uint32_t chunk_step = blocked ? 256u * BITS : 16u * BITS;
   const int64_t code_bytes = (int64_t)K * ABITS / 8;
 
   // row group q of this workgroup: rows (blockIdx.x * NG + q) * 16 + 0..15
@@ -99,7 +102,9 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     nrow[q] = n;
     nvalid[q] = n < N;
     const int nn = nvalid[q] ? n : 0;
-    wlane[q] = nvalid[q] ? (uint32_t)(n * row_bytes) + (uint32_t)(g * 4 * BITS) : kOffNone;
+    wlane[q] = !nvalid[q] ? kOffNone
+               : blocked ? (uint32_t)((n - nl) * row_bytes) + (uint32_t)(lane * 4 * BITS)
+                         : (uint32_t)(n * row_bytes) + (uint32_t)(g * 4 * BITS);
     if constexpr (LT) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -165,7 +170,7 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
       for (int q = 0; q < NG; ++q)
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-          buf_load<4 * BITS>(wres[w], ok ? wlane[q] : kOffNone, d.w[q][w], (uint32_t)(c * 128 * BITS / 8));
+          buf_load<4 * BITS>(wres[w], ok ? wlane[q] : kOffNone, d.w[q][w], (uint32_t)c * chunk_step);
       const uint32_t cs = (uint32_t)(c * 128 * ABITS / 8);
 #pragma unroll
       for (int s = 0; s < MSUB; ++s) {
@@ -299,7 +304,7 @@ static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStrea
                      (LT ? (size_t)NG * NW * PairTab<BITS>::NE * 16 * sizeof(uint32_t) : 0);
   hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG, LT>), grid, dim3(64 * splitk), lds,
                      stream, a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows,
-                     a.N, a.K, splitk, max_rows, a.out, a.ldo);
+                     a.N, a.K, splitk, max_rows, a.blocked, a.out, a.ldo);
   return hipGetLastError();
 }
 

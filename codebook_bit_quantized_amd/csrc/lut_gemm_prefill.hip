@@ -39,7 +39,8 @@ template <int BITS, int ABITS, bool LT>
 struct TileCtx {
   __amdgpu_buffer_rsrc_t wres[2];   // this expert's index block of each matrix
   __amdgpu_buffer_rsrc_t cres;      // the activation codes
-  uint32_t wrow_off[2];             // byte offset of this lane's weight rows
+  uint32_t wrow_off[2];             // byte offset of this lane's first 32 indices of each matrix
+  uint32_t wstep;                   // bytes between a lane's index slices of consecutive steps
   uint32_t crow_off;                // byte offset of this thread's activation row
   bool nvalid[2];
   int nrow[2];
@@ -76,7 +77,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
     const bool kok = live && kb < K;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      buf_load<4 * BITS>(c.wres[s], (c.nvalid[s] && kok) ? c.wrow_off[s] + (uint32_t)(kb * BITS / 8) : kOffNone, w[s]);
+      buf_load<4 * BITS>(c.wres[s], (c.nvalid[s] && kok) ? c.wrow_off[s] + (uint32_t)kt * c.wstep : kOffNone, w[s]);
     const int ka = kt * BK;
     const bool ok0 = live && c.avalid, ok1 = ok0 && ka + 32 < K;
     const uint32_t ab = c.crow_off + (uint32_t)(ka * ABITS / 8);
@@ -246,7 +247,7 @@ __global__ void __launch_bounds__(256, 1)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
-                    void* __restrict__ out, int64_t ldo) {
+                    int blocked, void* __restrict__ out, int64_t ldo) {
   // LDS pair tables: per wave, two matrix slots of 32 rows, NE entries each
   constexpr int NE = LT ? PairTab<BITS>::NE : 1;
   __shared__ __attribute__((aligned(16))) uint32_t Tab[LT ? 4 * 2 * NE * 32 : 1];
@@ -335,7 +336,11 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   if constexpr (NW == 2) { c.nrow[0] = c.nrow[1] = n0 + wave * 32 + c.nl; }   // gate, up
   else { c.nrow[0] = n0 + wave * 64 + c.nl; c.nrow[1] = c.nrow[0] + 32; }
   constexpr int L = 1 << BITS;
-  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  // bytes per row of the expert's index block (rows layout: each row's bitstream; blocked
+  // layout: 16-row x 128-channel tiles of 256*BITS bytes, a step of 64 channels being half
+  // a tile, so 128*BITS bytes apart in either half)
+  const int64_t row_bytes = index_row_bytes(K, BITS, blocked != 0);
+  c.wstep = blocked ? 128u * BITS : 8u * BITS;
   c.ptab = Tab;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -355,7 +360,9 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
       c.tab[s].load(W.codebook + rowi * L);
     }
     c.wres[s] = make_rsrc(W.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
-    c.wrow_off[s] = (uint32_t)((c.nvalid[s] ? c.nrow[s] : 0) * row_bytes);
+    const int nr = c.nvalid[s] ? c.nrow[s] : 0;
+    c.wrow_off[s] = blocked ? (uint32_t)((nr & ~15) * row_bytes) + (uint32_t)((c.g * 16 + (nr & 15)) * 4 * BITS)
+                            : (uint32_t)(nr * row_bytes) + (uint32_t)(c.g * 4 * BITS);
   }
 
   // output buffer: every row of this call (n_rows) x ldo elements
@@ -382,11 +389,11 @@ static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) 
   if (a.n_w == 2)
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT>), grid, dim3(256), 0, stream, a.codes,
                        a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                       min_rows, a.out, a.ldo);
+                       min_rows, a.blocked, a.out, a.ldo);
   else
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT>), grid, dim3(256), 0, stream, a.codes,
                        a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                       min_rows, a.out, a.ldo);
+                       min_rows, a.blocked, a.out, a.ldo);
   return hipGetLastError();
 }
 

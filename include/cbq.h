@@ -69,12 +69,19 @@ enum {
 
 #define CBQ_AUTO_MAX_LUT_ROWS 32
 
+/* Index layouts of cbq_weights.idx */
+enum {
+  CBQ_LAYOUT_ROWS = 0,     /* one LSB-first bitstream per row (the format the method defines) */
+  CBQ_LAYOUT_BLOCKED = 1   /* the same index bits regrouped by cbq_prepack_weights */
+};
+
 /*
  * One weight matrix type for E experts (E = 1 for a dense linear).
  * Reading of CodeQuant2, Figure 3 (right): a centroid matrix with one codebook per
  * weight row and a per-row assignment of every weight to one of its centroids.
- *  idx      : [E][N][K*bits/8] bytes.  Row n of expert e is an LSB-first bitstream:
- *             the index of weight k occupies bits [k*bits, (k+1)*bits).
+ *  idx      : layout CBQ_LAYOUT_ROWS: [E][N][K*bits/8] bytes.  Row n of expert e is an
+ *             LSB-first bitstream: the index of weight k occupies bits [k*bits, (k+1)*bits).
+ *             Layout CBQ_LAYOUT_BLOCKED: see cbq_prepack_weights.
  *  codebook : [E][N][1 << bits] fp16 bit patterns; entry c of row n is the value
  *             of every weight of that row whose index is c (order not assumed).
  *  W[e][n][k] = codebook[e][n][idx(e, n, k)].
@@ -84,7 +91,31 @@ typedef struct {
   const uint8_t* idx;
   const uint16_t* codebook;
   int32_t E, N, K, bits;
+  int32_t layout;          /* CBQ_LAYOUT_* */
 } cbq_weights;
+
+/*
+ * cbq_prepack_weights - regroup a weight set's indices for the GEMM kernels (an offline
+ * step, like the codebook construction).  The values are unchanged: W[e][n][k] is the
+ * same matrix, so the GEMM's results are those of the row layout (up to fp32 summation
+ * order, which does not change either).
+ *
+ * CBQ_LAYOUT_BLOCKED: with Kp = K rounded up to a multiple of 128, rows are taken in
+ * groups of 16 and channels in chunks of 128; the 32 indices of row 16G + r, channels
+ * 128c + 32j .. 128c + 32j + 31, are the 4*bits bytes of that row's bitstream at
+ * channel 128c + 32j (zeros past K), stored at byte
+ *     ((e * N/16 + G) * Kp/128 + c) * 256*bits + (16j + r) * 4*bits.
+ * So one 16-row x 128-channel tile is 256*bits contiguous bytes, which a 64-lane wave
+ * reads in one fully coalesced load (a row stream would give it sixteen 16*bits-byte
+ * pieces 1/8 K*bits bytes apart).
+ *
+ *  src : a CBQ_LAYOUT_ROWS weight set (device pointers).
+ *  dst : device buffer of cbq_prepack_bytes(src) bytes, 16-byte aligned, not
+ *        overlapping src->idx.  The blocked weight set is {dst, src->codebook, E, N, K,
+ *        bits, CBQ_LAYOUT_BLOCKED}.
+ */
+size_t cbq_prepack_bytes(const cbq_weights* src);
+int cbq_prepack_weights(const cbq_weights* src, uint8_t* dst, void* stream);
 
 /*
  * cbq_rotate_quantize - Hadamard rotation fused with per-token absmax quantisation.

@@ -134,8 +134,8 @@ def test_route_validation():
     assert rn(P, 4, 8, 2, 1, 0, P, P, None, P, P, None) == cbq.CBQ_EINVAL              # null offsets
 
 
-def _w(E=1, N=64, K=256, bits=4, idx=0x1000, cb=0x2000):
-    return cbq.cbq_weights(idx, cb, E, N, K, bits)
+def _w(E=1, N=64, K=256, bits=4, idx=0x1000, cb=0x2000, layout=0):
+    return cbq.cbq_weights(idx, cb, E, N, K, bits, layout)
 
 
 def _gemm(lib, W, n_w=1, act_bits=4, n_rows=4, epi=0, path=0, out=0x3000, ldo=64, codes=0x4000):
@@ -171,6 +171,26 @@ def test_gemm_validation():
     assert _gemm(lib, [_w()], codes=0x4004) == E                  # misaligned codes
     assert _gemm(lib, [_w()], n_rows=0) == cbq.CBQ_OK             # empty: no-op
     assert lib.cbq_gemm_workspace(ctypes.pointer(_w()), 1, 16, 4, 0) == 0
+    assert _gemm(lib, [_w(layout=2)]) == E                        # unknown layout
+    assert _gemm(lib, [_w(), _w(layout=1)], n_w=2, epi=1) == E    # gate/up layouts differ
+    assert _gemm(lib, [_w(layout=1)], n_rows=0) == cbq.CBQ_OK
+
+
+def test_prepack_validation():
+    lib = _lib()
+    E = cbq.CBQ_EINVAL
+    # blocked bytes: K rounded up to 128 channels
+    assert lib.cbq_prepack_bytes(ctypes.pointer(_w(E=2, N=64, K=256, bits=4))) == 2 * 64 * 256 // 2
+    assert lib.cbq_prepack_bytes(ctypes.pointer(_w(E=1, N=16, K=160, bits=3))) == 16 * 256 * 3 // 8
+    assert lib.cbq_prepack_bytes(ctypes.pointer(_w(E=3, N=2048, K=1408, bits=2))) == 3 * 2048 * 1408 // 4
+    assert lib.cbq_prepack_bytes(ctypes.pointer(_w(K=100))) == 0
+    pp = lib.cbq_prepack_weights
+    dst = ctypes.c_void_p(0x100000)
+    assert pp(ctypes.pointer(_w()), None, None) == E                       # null dst
+    assert pp(ctypes.pointer(_w()), ctypes.c_void_p(0x100004), None) == E  # misaligned dst
+    assert pp(ctypes.pointer(_w(layout=1)), dst, None) == E               # already blocked
+    assert pp(ctypes.pointer(_w(idx=0x1000)), ctypes.c_void_p(0x1000), None) == E  # overlap
+    assert pp(ctypes.pointer(_w(bits=5)), dst, None) == cbq.CBQ_EUNSUPPORTED
 
 
 def test_combine_validation():

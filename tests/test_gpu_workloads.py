@@ -11,6 +11,8 @@ class and choose_path rule), so what is checked here is what the benchmark times
   GPU's own input to that stage (the h codes come from the GPU's bf16 h, the down
   GEMM reads the GPU's h codes, combine reads the GPU's expert outputs).
 * Dense linears are small enough to compare every output.
+* The weights are regrouped into the blocked index layout, as the benchmark runs them;
+  the oracle reads the row layout they were generated in.
 * The free-running comparison (oracle end to end from x) is run where the oracle
   finishes in seconds; it reports the h-code flips that near-ties cause.
 
@@ -40,6 +42,11 @@ import bench  # noqa: E402
 N_SAMPLES = 1500
 
 
+def bench_weights(ws):
+    """The device weights the benchmark times: the blocked index layout."""
+    return bench.upload_weights(cbq, torch, ws)
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -57,7 +64,7 @@ def moe_setup(name):
         torch.cuda.empty_cache()
         wl = datagen.WORKLOADS[name]
         g, u, d = datagen.moe_weights(wl)
-        W = dict(gate=upload_weights(g), up=upload_weights(u), down=upload_weights(d))
+        W = dict(gate=bench_weights(g), up=bench_weights(u), down=bench_weights(d))
         _CACHE[name] = (wl, dict(gate=g, up=u, down=d), W)
     return _CACHE[name]
 
@@ -162,7 +169,7 @@ def test_dense256_full():
     T = wl.T_list[0]
     x = datagen.dense_tokens(wl, T)
     codes, scales = cbq.rotate_quantize(bf16_dev(x), wl.act_bits)
-    y = cbq.codebook_lut_gemm(codes, scales, wl.act_bits, [upload_weights(ws)])
+    y = cbq.codebook_lut_gemm(codes, scales, wl.act_bits, [bench_weights(ws)])
     torch.cuda.synchronize()
     rq = oracle.rotate_quantize(x, 0, wl.act_bits)
     assert np.array_equal(codes.cpu().numpy(), rq["codes"])
@@ -181,7 +188,7 @@ def dense_setup(which):
         wl = datagen.WORKLOADS["dense2560x9728"]
         ws = datagen.dense_weights(wl, which)
         Wd = oracle.dequantize(oracle.unpack_indices(ws.idx[0], ws.K, ws.bits), ws.codebook[0])
-        _DENSE[which] = (wl, ws, upload_weights(ws), Wd)
+        _DENSE[which] = (wl, ws, bench_weights(ws), Wd)
     return _DENSE[which]
 
 
