@@ -52,7 +52,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t* 
 
 // LT: weights looked up in LDS pair tables (2- and 3-bit codebooks), shared by the
 // workgroup's waves (they serve the same rows); otherwise in per-row register tables.
-template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT>
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH>
 __global__ void __launch_bounds__(NW == 2 ? 512 : 1024, BITS <= 3 ? 4 : 3)
 lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
@@ -158,12 +158,13 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     }
     const int nsub = (int)min<int64_t>((me - mb + 15) >> 4, MSUB);
 
-    // ring of two chunks of raw data, loaded two chunks ahead
+    // ring of DEPTH chunks of raw data, loaded DEPTH chunks ahead: a wave of few chunks
+    // (the split-K waves of small grids) has all of its loads in flight at once
     struct Slot {
       uint32_t w[NG][NW][BITS];
       uint32_t a[MSUB][ABITS];
     };
-    Slot ring[2];
+    Slot ring[DEPTH];
     auto load = [&](int c, Slot& d) {
       const bool ok = c < c_end && c * 128 + g * 32 < K;
 #pragma unroll
@@ -233,16 +234,19 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
         }
       }
     };
-    load(c_begin, ring[0]);
-    load(c_begin + 1, ring[1]);
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) load(c_begin + i, ring[i]);
     int c = c_begin;
-    for (; c + 1 < c_end; c += 2) {
-      chunk(ring[0]);
-      load(c + 2, ring[0]);
-      chunk(ring[1]);
-      load(c + 3, ring[1]);
+    for (; c + DEPTH - 1 < c_end; c += DEPTH) {
+#pragma unroll
+      for (int i = 0; i < DEPTH; ++i) {
+        chunk(ring[i]);
+        load(c + DEPTH + i, ring[i]);
+      }
     }
-    if (c < c_end) chunk(ring[0]);
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i)
+      if (c + i < c_end) chunk(ring[i]);
 
     // ordered split-K reduction
     if (ksplit) {
@@ -296,13 +300,13 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   }
 }
 
-template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT>
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH>
 static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
   dim3 grid((unsigned)((a.N + 16 * NG - 1) / (16 * NG)), (unsigned)E);
   const size_t lds = (size_t)(splitk - 1) * NG * NW * MSUB * 64 * sizeof(f32x4) +
                      (LT ? (size_t)NG * NW * PairTab<BITS>::NE * 16 * sizeof(uint32_t) : 0);
-  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG, LT>), grid, dim3(64 * splitk), lds,
+  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG, LT, DEPTH>), grid, dim3(64 * splitk), lds,
                      stream, a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows,
                      a.N, a.K, splitk, max_rows, a.blocked, a.out, a.ldo);
   return hipGetLastError();
@@ -313,11 +317,21 @@ static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStrea
 // tables (32 VGPRs per row) keep one, as more registers would cost occupancy.
 static int decode_groups(int bits, int n_w) { return (n_w == 1 && bits <= 3) ? 2 : 1; }
 
+// Calls of at most 16 rows (no expert can hold more) take one 16-token sub-tile and a
+// deeper ring: six chunks for a single 4-bit matrix, four for the gate/up pair and for
+// two row groups (what the registers hold); larger calls two sub-tiles and two chunks.
 template <int BITS, int ABITS, bool LT>
 static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStream_t s) {
-  if (a.n_w == 2) return launch_t<BITS, ABITS, 2, 2, 1, LT>(a, max_rows, splitk, s);
-  if constexpr (BITS <= 3) return launch_t<BITS, ABITS, 1, 2, 2, LT>(a, max_rows, splitk, s);
-  else return launch_t<BITS, ABITS, 1, 2, 1, LT>(a, max_rows, splitk, s);
+  const bool small = a.n_rows <= 16;
+  if (a.n_w == 2)
+    return small ? launch_t<BITS, ABITS, 2, 1, 1, LT, 4>(a, max_rows, splitk, s)
+                 : launch_t<BITS, ABITS, 2, 2, 1, LT, 2>(a, max_rows, splitk, s);
+  if constexpr (BITS <= 3)
+    return small ? launch_t<BITS, ABITS, 1, 1, 2, LT, 4>(a, max_rows, splitk, s)
+                 : launch_t<BITS, ABITS, 1, 2, 2, LT, 2>(a, max_rows, splitk, s);
+  else
+    return small ? launch_t<BITS, ABITS, 1, 1, 1, LT, 6>(a, max_rows, splitk, s)
+                 : launch_t<BITS, ABITS, 1, 2, 1, LT, 2>(a, max_rows, splitk, s);
 }
 
 // 2- and 3-bit codebooks: LDS pair tables unless the register tables are asked for (the
