@@ -938,6 +938,36 @@ def main():
     t1 = time.perf_counter()
     dom.ev = None
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
+
+    # The same step with every GEMM on PATH_AUTO, as a layer that cannot read the routing
+    # counts on the host runs it: each call launches both paths' grids and every expert
+    # goes to the LUT path (at most 32 rows) or the MFMA path on the device.  Timed after
+    # the main loop, outside it.
+    # The comparison takes the host-chosen paths again right after, with no events in the
+    # loop, so both sides run under the same clocks.
+    auto_info = None
+    if wl.kind == "moe":
+        def timed_loop():
+            for _ in range(args.warmup):
+                run_step()
+            torch.cuda.synchronize()
+            ta = time.perf_counter()
+            for _ in range(args.steps):
+                run_step()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - ta) * 1000.0 / args.steps
+
+        saved = [(p.path_gu, p.path_dn) for p in phases]
+        for p in phases:
+            p.path_gu = p.path_dn = cbq.PATH_AUTO | tflag
+        auto_ms = timed_loop()
+        for p, (gu, dn) in zip(phases, saved):
+            p.path_gu, p.path_dn = gu, dn
+        host_ms = timed_loop()
+        auto_info = dict(ms_per_step=round(auto_ms, 4),
+                         tokens_per_s=round(sum(p.T for p in phases) / (auto_ms / 1000.0), 1),
+                         host_choice_ms_per_step=round(host_ms, 4),
+                         extra_ms_vs_host_choice=round(auto_ms - host_ms, 4))
     tokens = sum(p.T for p in phases)
     value = tokens / (ms_per_step / 1000.0)
     dom_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(start_evs, end_evs)]))
@@ -1018,7 +1048,8 @@ def main():
     line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,
-                roofline=roofline, decode_roofline=decode_info, cpu_baseline=cpu,
+                roofline=roofline, decode_roofline=decode_info, auto_path_step=auto_info,
+                cpu_baseline=cpu,
                 setup_s=round(setup_s, 1), host=platform.node())
     print(json.dumps(line))
 

@@ -20,6 +20,8 @@
 //
 // A tile is one column range x the y-th 256-row slice in expert order, skipping
 // experts with at most min_rows rows (those go to the decode path).
+#include <algorithm>
+
 #include "cbq_internal.hpp"
 
 namespace cbq {
@@ -383,7 +385,10 @@ template <int BITS, int ABITS, bool LT>
 static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
   const int ncol = a.n_w == 2 ? 128 : 256;
-  int64_t mtiles = (a.n_rows + BM - 1) / BM + (a.offsets ? E : 0);   // M-tile slots
+  // M-tile slots: an expert of r rows takes ceil(r / BM) <= r / BM + 1 of them, and only
+  // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them
+  const int64_t big = a.offsets ? std::min<int64_t>(E, a.n_rows / (min_rows + 1)) : 0;
+  int64_t mtiles = (a.n_rows + BM - 1) / BM + big;
   mtiles = (mtiles + 15) / 16 * 16;                  // a multiple of 16 (XCD pairs)
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
