@@ -74,6 +74,23 @@ class CacheFlush:
             self.buf.sum()
 
 
+def cold_us(torch, flush, fn, reps):
+    """Median time in us of fn() over reps launches, each after flush() (caches cold)."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) * 1000.0)
+    return float(np.median(ts))
+
+
 def upload_weights(cbq, torch, ws, layout="blocked", dev="cuda:0"):
     """A host weight set on the device, regrouped into the blocked index layout
     (cbq_prepack_weights) unless layout == "rows"."""
@@ -170,6 +187,12 @@ class MoEPhase:
                                    expert_offsets=self.rt["offsets"],
                                    row_token=self.rt["sorted_tokens"], path=self.path_gu,
                                    out=self.h)
+
+
+    def gemm_dn_only(self):
+        self.cbq.codebook_lut_gemm(self.codes_h, self.scales_h, self.wl.act_bits, [self.W["down"]],
+                                   n_rows=self.R, expert_offsets=self.rt["offsets"],
+                                   path=self.path_dn, out=self.out)
 
 
 def run_mixed_step(torch, phases, side=None):
@@ -664,20 +687,6 @@ def bench_decode_table(args, cbq, torch):
     dev = "cuda:0"
     flush = CacheFlush(torch, dev, args.flush)
 
-    def cold_us(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            flush()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            torch.cuda.synchronize()
-            ts.append(s.elapsed_time(e) * 1000.0)
-        return float(np.median(ts))
-
     def entry(label, T, nbytes, us, **kw):
         gbs = nbytes / (us * 1e-6) / 1e9
         return dict(gemm=label, tokens=T, algorithmic_bytes=int(nbytes), median_us=round(us, 2),
@@ -697,8 +706,8 @@ def bench_decode_table(args, cbq, torch):
                     xt = torch.from_numpy(datagen.dense_tokens(wl, T, which).view(np.int16)).to(dev)
                     codes, scales = cbq.rotate_quantize(xt.view(torch.bfloat16), a)
                     out = torch.empty((T, N), dtype=torch.float32, device=dev)
-                    us = cold_us(lambda: cbq.codebook_lut_gemm(codes, scales, a, [Wd],
-                                                               path=cbq.PATH_LUT, out=out), reps)
+                    us = cold_us(torch, flush, lambda: cbq.codebook_lut_gemm(codes, scales, a, [Wd],
+                                                                             path=cbq.PATH_LUT, out=out), reps)
                     nbytes = wbytes + T * (K * a // 8 + 4) + T * N * 4
                     rows.append(entry(f"dense {K}->{N}", T, nbytes, us, act_bits=a, bits=wl.bits,
                                       layout=layout))
@@ -717,7 +726,7 @@ def bench_decode_table(args, cbq, torch):
                     ph.run()
                     torch.cuda.synchronize()
                     counts = np.diff(ph.rt["offsets"].cpu().numpy().astype(np.int64))
-                    us = cold_us(ph.gemm_gu_only, reps)
+                    us = cold_us(torch, flush, ph.gemm_gu_only, reps)
                     rows.append(entry(f"{name} gate/up+SwiGLU", T, gate_up_bytes(wl, counts, T), us,
                                       act_bits=wl.act_bits, bits=wl.bits_gate_up, tables=tname,
                                       layout=layout,
@@ -726,6 +735,48 @@ def bench_decode_table(args, cbq, torch):
     del flush
     print(json.dumps(dict(mode="decode_table", cache_flush=args.flush, peak_GBs=HBM_PEAK_GBS,
                           reps=reps, results=rows)))
+
+
+def down_bytes(wl, counts, R):
+    """Algorithmic HBM bytes of one down launch: each active expert's indices + codebooks
+    once, the h codes and scales of every row once, the fp32 output once."""
+    per_matrix = wl.H * wl.F * wl.bits_down // 8 + wl.H * (1 << wl.bits_down) * 2
+    return per_matrix * int((counts > 0).sum()) + R * (wl.F * wl.act_bits // 8 + 4) + R * wl.H * 4
+
+
+def bench_lut_forms(args, cbq, torch):
+    """The 128-expert layer's decode GEMMs (gate/up with SwiGLU, and down) on the
+    register-table LUT path and on the pages' two table forms (per-row product tables
+    with sign folding; per-row integer buckets of the activation codes), cold (caches
+    flushed) and warm, at the decode batches given by --forms-tokens."""
+    dev = "cuda:0"
+    flush = CacheFlush(torch, dev, args.flush)
+    wl = datagen.WORKLOADS["moe128_h2048_f768"]
+    host = datagen.moe_weights(wl)
+    W = dict(zip(("gate", "up", "down"), (upload_weights(cbq, torch, w, args.layout, dev) for w in host)))
+    forms = (("lut_reg_tables", cbq.PATH_LUT), ("pages_products", cbq.PATH_PAGES_PRODUCTS),
+             ("pages_buckets", cbq.PATH_PAGES_BUCKETS))
+    reps = max(5, args.decode_reps)
+    rows = []
+    for T in (int(t) for t in args.forms_tokens.split(",")):
+        x, lg = datagen.moe_tokens(wl, T)
+        for name, path in forms:
+            ph = MoEPhase(cbq, torch, wl, W, x, lg, path, path)
+            ph.run()
+            torch.cuda.synchronize()
+            counts = np.diff(ph.rt["offsets"].cpu().numpy().astype(np.int64))
+            for gemm, fn, nbytes in (("gate/up+SwiGLU", ph.gemm_gu_only, gate_up_bytes(wl, counts, T)),
+                                     ("down", ph.gemm_dn_only, down_bytes(wl, counts, ph.R))):
+                cold = cold_us(torch, flush, fn, reps)
+                warm = cold_us(torch, None, fn, reps)
+                gbs = nbytes / (cold * 1e-6) / 1e9
+                rows.append(dict(gemm=f"moe128_h2048_f768 {gemm}", form=name, tokens=T,
+                                 max_rows_per_expert=int(counts.max()),
+                                 algorithmic_bytes=int(nbytes), cold_us=round(cold, 2),
+                                 warm_us=round(warm, 2), cold_frac=round(gbs / HBM_PEAK_GBS, 4)))
+    del flush
+    print(json.dumps(dict(mode="lut_forms", cache_flush=args.flush, layout=args.layout,
+                          peak_GBs=HBM_PEAK_GBS, reps=reps, results=rows)))
 
 
 def bench_dense_rotation(args, cbq, torch):
@@ -813,6 +864,11 @@ def main():
     ap.add_argument("--decode-table", action="store_true",
                     help="cold HBM rooflines of every decode GEMM (dense T 1/4/16 with A4 and A8, "
                          "128-expert T 1/8/64, 64 + 2 expert T 32) instead")
+    ap.add_argument("--lut-forms", action="store_true",
+                    help="time the 128-expert decode GEMMs on the register-table LUT path and "
+                         "the two table forms (product tables, activation buckets) instead")
+    ap.add_argument("--forms-tokens", default="1,8,64",
+                    help="decode batches for --lut-forms (comma separated)")
     ap.add_argument("--crossover", action="store_true",
                     help="time the LUT and MFMA paths against rows per expert instead")
     ap.add_argument("--peaks", action="store_true",
@@ -864,6 +920,9 @@ def main():
         return
     if args.decode_table:
         bench_decode_table(args, cbq, torch)
+        return
+    if args.lut_forms:
+        bench_lut_forms(args, cbq, torch)
         return
     if args.dense_rotation:
         bench_dense_rotation(args, cbq, torch)

@@ -14,7 +14,7 @@ and ``moe_ffn``, which sequences them into one MoE FFN layer, and
 """
 from ._binding import (AUTO_MAX_LUT_ROWS, CBQ_EHIP, CBQ_EINVAL, CBQ_EUNSUPPORTED, CBQ_EWORKSPACE,
                        CBQ_OK, EPI_F32, EPI_SWIGLU_BF16, EXPORTED, LIB_PATH, PATH_AUTO, PATH_LUT,
-                       PATH_MFMA, PATH_REG_TABLES, PATH_LDS_TABLES, CbqError, CodebookWeights, cbq_weights, codebook_lut_gemm,
+                       PATH_MFMA, PATH_PAGES_PRODUCTS, PATH_PAGES_BUCKETS, PATH_REG_TABLES, PATH_LDS_TABLES, CbqError, CodebookWeights, cbq_weights, codebook_lut_gemm,
                        cpu_lut_gemm, kmeans_codebooks, load_library, moe_combine, moe_ffn, moe_route_gather,
                        moe_route_gather_noalloc, prepack_weights, LAYOUT_ROWS, LAYOUT_BLOCKED,
                        refit_codebooks,
@@ -27,6 +27,6 @@ __all__ = [
     "route_workspace", "kmeans_codebooks", "refit_codebooks", "cpu_lut_gemm", "rotate_quantize_dense",
     "rotate_dense_workspace",
     "CodebookWeights", "CbqError", "load_library", "LIB_PATH", "EXPORTED", "cbq_weights",
-    "EPI_F32", "EPI_SWIGLU_BF16", "PATH_AUTO", "PATH_LUT", "PATH_MFMA", "PATH_REG_TABLES", "PATH_LDS_TABLES", "AUTO_MAX_LUT_ROWS",
+    "EPI_F32", "EPI_SWIGLU_BF16", "PATH_AUTO", "PATH_LUT", "PATH_MFMA", "PATH_PAGES_PRODUCTS", "PATH_PAGES_BUCKETS", "PATH_REG_TABLES", "PATH_LDS_TABLES", "AUTO_MAX_LUT_ROWS",
     "CBQ_OK", "CBQ_EINVAL", "CBQ_EUNSUPPORTED", "CBQ_EWORKSPACE", "CBQ_EHIP",
 ]

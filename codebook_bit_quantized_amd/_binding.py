@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libcbq.so")
 CBQ_OK, CBQ_EINVAL, CBQ_EUNSUPPORTED, CBQ_EWORKSPACE, CBQ_EHIP = 0, -1, -2, -3, -4
 EPI_F32, EPI_SWIGLU_BF16 = 0, 1
 PATH_AUTO, PATH_LUT, PATH_MFMA = 0, 1, 2
+PATH_PAGES_PRODUCTS, PATH_PAGES_BUCKETS = 3, 4   # the table forms (4-bit, A4; never chosen by AUTO)
 PATH_REG_TABLES = 0x10   # flags: where 2-/3-bit codebooks are looked up (default: per path)
 PATH_LDS_TABLES = 0x20
 AUTO_MAX_LUT_ROWS = 32

@@ -236,7 +236,13 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   if (tflags == (CBQ_PATH_REG_TABLES | CBQ_PATH_LDS_TABLES))
     return fail(CBQ_EINVAL, "CBQ_PATH_REG_TABLES and CBQ_PATH_LDS_TABLES exclude each other");
   path &= ~(CBQ_PATH_REG_TABLES | CBQ_PATH_LDS_TABLES);
-  if (path < CBQ_PATH_AUTO || path > CBQ_PATH_MFMA) return fail(CBQ_EINVAL, "unknown path %d", path);
+  if (path < CBQ_PATH_AUTO || path > CBQ_PATH_PAGES_BUCKETS) return fail(CBQ_EINVAL, "unknown path %d", path);
+  const bool pages = path == CBQ_PATH_PAGES_PRODUCTS || path == CBQ_PATH_PAGES_BUCKETS;
+  if (pages && tflags) return fail(CBQ_EINVAL, "table flags apply to CBQ_PATH_AUTO, CBQ_PATH_LUT and CBQ_PATH_MFMA only");
+  if (pages && (W[0].bits != 4 || act_bits != 4))
+    return fail(CBQ_EUNSUPPORTED, "the table paths take 4-bit codebooks and act_bits == 4 (got bits %d, act_bits %d)",
+                W[0].bits, act_bits);
+  if (pages && W[0].K > 16384) return fail(CBQ_EUNSUPPORTED, "the table paths take K <= 16384 (got %d)", W[0].K);
   if (n_rows < 0) return fail(CBQ_EINVAL, "n_rows must be >= 0");
   if (n_rows > 0x7FFFFFFF) return fail(CBQ_EUNSUPPORTED, "n_rows must be < 2^31");
   if (ldo < W[0].N || ldo % 4) return fail(CBQ_EINVAL, "ldo must be >= N and a multiple of 4 (got %lld)", (long long)ldo);
@@ -271,6 +277,8 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
     e = cbq::launch_lut_decode(a, -1, s);
   } else if (path == CBQ_PATH_MFMA) {
     e = cbq::launch_mfma_prefill(a, 0, s);
+  } else if (pages) {
+    e = cbq::launch_lut_pages(a, path == CBQ_PATH_PAGES_PRODUCTS ? 0 : 1, s);
   } else {
     e = cbq::launch_lut_decode(a, CBQ_AUTO_MAX_LUT_ROWS, s);
     if (e == hipSuccess && n_rows > CBQ_AUTO_MAX_LUT_ROWS)

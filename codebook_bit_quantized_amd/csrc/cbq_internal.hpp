@@ -56,6 +56,10 @@ hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream
 // MFMA (prefill) path.  Experts with at most min_rows rows are skipped (AUTO split).
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream);
 
+// The pages' table forms (4-bit codebooks, A4): mode 0 per-row product tables with sign
+// folding, mode 1 per-row integer buckets of the activation codes.
+hipError_t launch_lut_pages(const GemmArgs& a, int mode, hipStream_t stream);
+
 // Regroups a row-layout index block [E][N][K*bits/8] into the blocked layout.
 hipError_t launch_prepack(const uint8_t* src, uint8_t* dst, int E, int N, int K, int bits,
                           hipStream_t stream);

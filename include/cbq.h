@@ -54,9 +54,20 @@ enum {
   CBQ_PATH_LUT = 1,   /* register codebook lookup feeding 16x16x32 MFMA; an expert's weights
                          are streamed from HBM once (K split over waves for experts of at most
                          32 rows, row blocks of 32 split over waves for larger ones) */
-  CBQ_PATH_MFMA = 2   /* 256-row tiles: weights dequantised in registers straight into the
+  CBQ_PATH_MFMA = 2,  /* 256-row tiles: weights dequantised in registers straight into the
                          B operand of 32x32x16 fp16 MFMAs, activation codes converted to fp16
                          once per tile step in LDS */
+  /* The table forms of CodeQuant2, Figure 4 (a table built once, then products read from
+     shared memory instead of multiplied; the AI Radio episode, "Improvements", calls it a
+     multiplication table).  4-bit codebooks, act_bits == 4 and K <= 16384 only (else
+     CBQ_EUNSUPPORTED), no table flags; meant for experts of a few rows, correct for any.  Never chosen by
+     CBQ_PATH_AUTO: kept to measure them against CBQ_PATH_LUT. */
+  CBQ_PATH_PAGES_PRODUCTS = 3, /* per weight row, an LDS table of the products |a| * C[c] of
+                                  the nine code magnitudes and 16 centroids, exact in fp32;
+                                  the code's sign applied after the lookup; fp32 sums */
+  CBQ_PATH_PAGES_BUCKETS = 4   /* per weight row and token, 16 integer buckets in LDS that
+                                  sum the activation codes by weight index, then
+                                  sum_c C[c] * bucket[c] (fp64, rounded to fp32 per lane) */
 };
 
 /* Flags added to a path to choose where 2- and 3-bit codebooks are looked up (4-bit ones
@@ -269,8 +280,10 @@ int cbq_moe_route_gather_noalloc(const float* logits, int64_t T, int32_t E, int3
  *  epilogue        : CBQ_EPI_F32 (n_w == 1): out[r][n] = scale[t_r] * sum_k q[t_r][k] W[e][n][k]
  *                    as fp32.  CBQ_EPI_SWIGLU_BF16 (n_w == 2): g, u as above, then
  *                    out[r][n] = bf16_rne(silu(g) * u).
- *  path            : CBQ_PATH_AUTO / CBQ_PATH_LUT / CBQ_PATH_MFMA.  Products are exact
- *                    on every path; the paths differ only in the fp32 summation order.
+ *  path            : CBQ_PATH_AUTO / CBQ_PATH_LUT / CBQ_PATH_MFMA, optionally with one
+ *                    table flag, or CBQ_PATH_PAGES_PRODUCTS / CBQ_PATH_PAGES_BUCKETS.
+ *                    Products are exact on every path; the paths differ only in the
+ *                    fp32 summation order.
  *                    The SwiGLU epilogue is one fp32 formula on every path
  *                    (g * u * rcp(1 + exp(-g)) with the hardware exp2 and reciprocal),
  *                    so the bf16 h of two paths differs only where that summation

@@ -160,7 +160,13 @@ def test_gemm_validation():
     assert _gemm(lib, [_w()], n_w=1, epi=1) == E                  # SwiGLU needs two
     assert _gemm(lib, [_w(), _w(N=128)], n_w=2, epi=1) == E       # mismatched gate/up
     assert _gemm(lib, [_w()], epi=7) == E
-    assert _gemm(lib, [_w()], path=3) == E
+    assert _gemm(lib, [_w()], path=5) == E
+    # the table forms take 4-bit codebooks and A4 only, and no table flags
+    assert _gemm(lib, [_w(bits=3)], path=cbq.PATH_PAGES_PRODUCTS) == cbq.CBQ_EUNSUPPORTED
+    assert _gemm(lib, [_w()], act_bits=8, path=cbq.PATH_PAGES_BUCKETS) == cbq.CBQ_EUNSUPPORTED
+    assert _gemm(lib, [_w()], path=cbq.PATH_PAGES_PRODUCTS | cbq.PATH_REG_TABLES) == E
+    assert _gemm(lib, [_w()], path=cbq.PATH_PAGES_BUCKETS | cbq.PATH_LDS_TABLES) == E
+    assert _gemm(lib, [_w()], path=cbq.PATH_PAGES_BUCKETS, n_rows=0) == cbq.CBQ_OK
     assert _gemm(lib, [_w()], path=cbq.PATH_LUT | 0x40) == E     # unknown flag
     assert _gemm(lib, [_w()], path=cbq.PATH_LUT | cbq.PATH_REG_TABLES | cbq.PATH_LDS_TABLES) == E
     assert _gemm(lib, [_w()], path=cbq.PATH_MFMA | cbq.PATH_LDS_TABLES, n_rows=0) == cbq.CBQ_OK

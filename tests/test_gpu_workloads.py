@@ -218,7 +218,8 @@ def test_moe128_decode_layer(T):
     x, lg = datagen.moe_tokens(wl, T)
     ph, path = run_bench_phase(wl, W, x, lg, decode=True)
     assert path == cbq.PATH_LUT
-    check_moe_phase(wl, host, ph, x, lg, seed=100 + T, extra_paths=(cbq.PATH_MFMA,))
+    check_moe_phase(wl, host, ph, x, lg, seed=100 + T,
+                    extra_paths=(cbq.PATH_MFMA, cbq.PATH_PAGES_PRODUCTS, cbq.PATH_PAGES_BUCKETS))
 
 
 def _flips(ph, ref):
