@@ -56,16 +56,20 @@ __device__ __forceinline__ float xor_lane_f32(float v) {
   return __builtin_bit_cast(float, xor_lane<M>(__builtin_bit_cast(int, v)));
 }
 
-// one butterfly stage between lanes j and j ^ M (M lanes = 32 * M channels apart):
-// the lower lane keeps p + v, the upper one p + (-v), the sign flipped by one xor on
-// the high word instead of a select between two sums
+// one butterfly stage between lanes j and j ^ M (M lanes = 32 * M channels apart): the
+// lower lane keeps v + p, the upper one v - p, which is the negative of the butterfly's
+// p - v.  Each value is one fma(p, +-1, v) accumulating into v (the product by +-1 is
+// exact, so it rounds the same sum an add would).  Partners always carry the same sign
+// (they differ only in the stage's own lane bit), so after the lane stages a lane's
+// values are the transform times (-1)^(number of upper stages), i.e. the parity of its
+// lane bits inside the block; the quantiser takes that sign into its multiplier.
 template <int M>
 __device__ __forceinline__ void lane_stage(double* v, bool upper) {
-  const uint64_t smask = upper ? 0x8000000000000000ull : 0ull;
+  const double sgn = upper ? -1.0 : 1.0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const double p = xor_lane_f64<M>(v[i]);
-    v[i] = p + __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, v[i]) ^ smask);
+    v[i] = __builtin_fma(p, sgn, v[i]);
   }
 }
 
@@ -224,7 +228,7 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const double p = xchg[i * npad + (tid ^ m)];
-        v[c + i] = upper ? (p - v[c + i]) : (v[c + i] + p);
+        v[c + i] += upper ? -p : p;       // upper lanes keep the negated butterfly
       }
     }
   }
@@ -266,15 +270,25 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
   }
 
   // ---- quantise: s = M / Q, q = clamp(rint(fp32(v / s))) ----
+  // rint by the magic-number add: r + 1.5 * 2^23 rounds r (|r| <= 128) to the nearest
+  // integer, ties to even, and leaves q = rint(r) in the low bits of the sum's pattern
+  // (0x4B400000 + q); the clamp is applied to the sum, whose bounds are exact, and the
+  // codes are packed from those low bits
   const float Q = act_bits == 4 ? 7.0f : 127.0f;
   const float lo = act_bits == 4 ? -8.0f : -127.0f;
+  constexpr float kMagic = 12582912.0f;
   const float s = amax / Q;
-  const double rs = amax > 0.0f ? 1.0 / (double)s : 0.0;
-  int q[32];
+  // the lane's values carry the sign (-1)^popcount(its lane bits inside the block) from
+  // the lane stages: fold it into the (exactly negated) multiplier, so fp32(u * rs) is the
+  // quotient of the transform itself and the clamp sees the right sign
+  const int gth_q = b >> 5;
+  const bool neg = gth_q > 1 && (__builtin_popcount((unsigned)j & (unsigned)(gth_q - 1)) & 1);
+  const double rs = amax > 0.0f ? (neg ? -1.0 : 1.0) / (double)s : 0.0;
+  uint32_t q[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float r = rintf((float)((double)u[i] * rs));
-    q[i] = (int)__builtin_amdgcn_fmed3f(r, lo, Q);
+    const float r = (float)((double)u[i] * rs);
+    q[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(r + kMagic, kMagic + lo, kMagic + Q));
   }
   if (active) {
     if (act_bits == 4) {
@@ -283,7 +297,7 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
       for (int k = 0; k < 4; ++k) {
         uint32_t d = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d |= ((uint32_t)q[8 * k + i] & 0xFu) << (4 * i);
+        for (int i = 0; i < 8; ++i) d |= (q[8 * k + i] & 0xFu) << (4 * i);
         w[k] = d;
       }
       *reinterpret_cast<u32x4*>(codes + t * (K / 2) + (int64_t)j * 16) = u32x4{w[0], w[1], w[2], w[3]};
@@ -293,7 +307,7 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
       for (int k = 0; k < 8; ++k) {
         uint32_t d = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d |= ((uint32_t)q[4 * k + i] & 0xFFu) << (8 * i);
+        for (int i = 0; i < 4; ++i) d |= (q[4 * k + i] & 0xFFu) << (8 * i);
         w[k] = d;
       }
       u32x4* dst = reinterpret_cast<u32x4*>(codes + t * K + (int64_t)j * 32);
