@@ -10,15 +10,17 @@
 // the four waves.  Products are exact (int codes x fp16 centroids); only the fp32
 // summation order differs from the plain definition.
 //
-// Tile: up to 256 rows of one expert x 256 columns x 64 channels per step.  Wave w
-// owns 64 columns (for the gate/up pair: 32 gate rows and the same 32 up rows, so
-// the SwiGLU epilogue finds g and u in one lane) and all rows of the tile, held as
-// up to 8 x 2 accumulators of 32x32 (256 AGPRs, one wave per SIMD).  Only the
-// 32-row sub-tiles that hold rows are computed, so an expert's last tile wastes
-// fewer than 32 rows.  A is double-buffered in LDS and the next step's loads are
-// issued before this step's MFMAs.
+// Tile: up to 128 rows of one expert x 256 columns x 64 channels per step, four waves.
+// Wave w owns 64 columns (for the gate/up pair: 32 gate rows and the same 32 up rows,
+// so the SwiGLU epilogue finds g and u in one lane) and all rows of the tile, held as
+// up to 4 x 2 accumulators of 32x32 (128 registers); with 256 registers a wave, two
+// workgroups share each CU (two waves per SIMD), so one workgroup's epilogue, prologue
+// and waits overlap the other's MFMAs.  Only the 32-row sub-tiles that hold rows are
+// computed, so an expert's last tile wastes fewer than 32 rows.  A is double-buffered
+// in LDS (two threads convert each row's codes) and the next step's loads are issued
+// before this step's MFMAs.
 //
-// A tile is one column range x the y-th 256-row slice in expert order, skipping
+// A tile is one column range x the y-th 128-row slice in expert order, skipping
 // experts with at most min_rows rows (those go to the decode path).
 #include <algorithm>
 
@@ -27,10 +29,10 @@
 namespace cbq {
 
 namespace {
-constexpr int BM = 256;     // rows per tile
+constexpr int BM = 128;     // rows per tile (two threads convert each row's codes)
+constexpr int XG = 2;       // consecutive M-tiles kept on one XCD
 constexpr int BK = 64;      // channels per step
 constexpr int LDW = BK + 8; // fp16 per LDS row (padding staggers the banks)
-constexpr int MSUB = BM / 32;
 
 }  // namespace
 
@@ -69,7 +71,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   // Raw loads run two steps ahead in a ring of two slots; the step loop is unrolled
   // by two so every slot index is a compile-time constant.
   uint32_t rw[2][2][BITS];     // [slot][matrix] raw indices
-  uint32_t ra[2][ABITS * 2];   // [slot] raw activation codes
+  uint32_t ra[2][ABITS];       // [slot] raw activation codes (this thread's half row)
   uint32_t bdA[2][16], bdB[2][16];  // dequantised weights, alternating between steps
   f16x8 af[NMS];               // A fragments of the current 16-channel sub-step
 
@@ -80,25 +82,19 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       buf_load<4 * BITS>(c.wres[s], (c.nvalid[s] && kok) ? c.wrow_off[s] + (uint32_t)kt * c.wstep : kOffNone, w[s]);
-    const int ka = kt * BK;
-    const bool ok0 = live && c.avalid, ok1 = ok0 && ka + 32 < K;
+    const int ka = kt * BK + 32 * (tid & 1);
+    const bool okh = live && c.avalid && ka < K;
     const uint32_t ab = c.crow_off + (uint32_t)(ka * ABITS / 8);
 #pragma unroll
-    for (int i = 0; i < ABITS / 4; ++i)       // first 32 codes
-      buf_load<16>(c.cres, ok0 ? ab + 16 * i : kOffNone, a + 4 * i);
-#pragma unroll
-    for (int i = 0; i < ABITS / 4; ++i)       // second 32 codes
-      buf_load<16>(c.cres, ok1 ? ab + 16 * (ABITS / 4 + i) : kOffNone, a + 4 * (ABITS / 4 + i));
+    for (int i = 0; i < ABITS / 4; ++i)       // this thread's 32 codes
+      buf_load<16>(c.cres, okh ? ab + 16 * i : kOffNone, a + 4 * i);
   };
   auto astore = [&](int buf, const uint32_t* a) {
     uint32_t d[16];
-    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][tid * LDW]);
+    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][(tid >> 1) * LDW]) + 4 * (tid & 1);
+    codes32_to_f16_ord<ABITS, LT>(a, d);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      codes32_to_f16_ord<ABITS, LT>(a + h * ABITS, d);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ap[h * 4 + j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
-    }
+    for (int j = 0; j < 4; ++j) ap[j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
   };
   auto frag = [&](int buf, int kk, int ms) {
     return *reinterpret_cast<const f16x8*>(&As[buf][(ms * 32 + nl) * LDW + g * 32 + kk * 8]);
@@ -127,19 +123,20 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
       for (int i = 0; i < 4; ++i) d[4 * j + i] = tmp[4 * (j & 1) + i];
     }
   };
-  // Piece p (0..7) of the activation conversion: codes 8p..8p+7 -> one 16-byte LDS store.
+  // Piece p (0..3) of this thread's half-row conversion: codes 8p..8p+7 of its 32 -> one
+  // 16-byte LDS store.
   auto a_piece = [&](int buf, const uint32_t* a, int p) {
     uint32_t d[4];
-    const int h = p >> 2, j = p & 3;
-    codes8_group<ABITS, LT>(a + h * ABITS, j, d);
-    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][tid * LDW]);
+    codes8_group<ABITS, LT>(a, p, d);
+    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][(tid >> 1) * LDW]) + 4 * (tid & 1);
     ap[p] = u32x4{d[0], d[1], d[2], d[3]};
   };
   // One step: MFMAs on LDS buffer `buf` with weights `bd`, while step kt+1 is
   // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
-  // (wf, af_raw) is refilled with step kt+2.  The preparation is cut into pieces that
-  // are placed between the MFMA pairs in program order (scheduling fences keep them
-  // there), so the vector ALU work issues while the matrix cores are busy.
+  // (wf, af_raw) is refilled with step kt+2.  The preparation is cut into 8 pieces (4 of
+  // activation conversion, 4 of the first matrix's dequantisation) placed between the
+  // MFMA pairs in program order (scheduling fences keep them there), so the vector ALU
+  // work issues while the matrix cores are busy.
   auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
                   uint32_t (&wn)[2][BITS], uint32_t* an, uint32_t (&wf)[2][BITS], uint32_t* af_raw) {
     gload(kt + 2, wf, af_raw);
@@ -156,9 +153,9 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
         af[ms] = frag(buf, kk + 1, ms);
         const int i = kk * NMS + ms;
 #pragma unroll
-        for (int p = (12 * i + PRE - 1) / PRE; p < (12 * (i + 1) + PRE - 1) / PRE; ++p) {
-          if (p < 8) a_piece(buf ^ 1, an, p);
-          else dq_piece(0, wn[0], bn[0], p - 8);
+        for (int p = (8 * i + PRE - 1) / PRE; p < (8 * (i + 1) + PRE - 1) / PRE; ++p) {
+          if (p < 4) a_piece(buf ^ 1, an, p);
+          else dq_piece(0, wn[0], bn[0], p - 4);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -245,7 +242,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
 }
 
 template <int BITS, int ABITS, int NW, bool LT>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
@@ -264,14 +261,14 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so XCD x
   // gets ids x, x + 8, ...; those ids work through rounds of gridDim.x column tiles
   // of one M-tile each, so the column tiles of an M-tile (same activation rows) share
-  // one L2.  Rounds 2P and 2P + 1 of XCD x take the M-tile pair (2s, 2s + 1),
-  // s = 8P + (x + P) % 8: consecutive M-tiles (usually of one expert: same weights)
-  // stay on one XCD, and the pair slot rotates with P to spread the work.  (The host
-  // makes the M-tile slots a multiple of 16.)
+  // one L2.  Rounds XG*P .. XG*P + XG - 1 of XCD x take the M-tiles XG*s .. XG*s + XG - 1,
+  // s = 8P + (x + P) % 8: runs of XG consecutive M-tiles (mostly of one expert: the same
+  // weights) stay on one XCD, and the slot rotates with P to spread the work.  (The host
+  // makes the M-tile slots a multiple of 8 * XG.)
   const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
   const uint32_t q = (lin / 8) / gridDim.x;
-  const uint32_t P = q / 2;
-  const int64_t ty = 2 * (8 * (int64_t)P + (lin % 8 + P) % 8) + (q & 1);
+  const uint32_t P = q / XG;
+  const int64_t ty = XG * (8 * (int64_t)P + (lin % 8 + P) % 8) + (q % XG);
   const int tcol = (int)((lin / 8) % gridDim.x);
   // ---- M-tile -> (expert, first row): wave 0 scans the experts' tile counts ----
   if (tid < 64) {
@@ -314,17 +311,26 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   c.K = K;
   c.tid = tid;
   c.rows = rows;
-  // ---- activation loader: thread t owns tile row t ----
-  c.avalid = tid < rows;
+  // ---- activation loader: threads 2i and 2i + 1 own the two 32-code halves of tile row i ----
+  const int arow = tid >> 1;                         // two threads per tile row
+  c.avalid = arow < rows;
   int64_t atok = 0;
   constexpr uint32_t ESZ = NW == 2 ? 2 : 4;
-  s_rowoff[tid] = kOffNone;
-  s_scale[tid] = 0.0f;
+  if (tid < BM) {                                    // thread t < BM: row t's scale and output offset
+    uint32_t ro = kOffNone;
+    float sv = 0.0f;
+    if (tid < rows) {
+      const int64_t r = r0 + m0 + tid;
+      const int64_t tk = row_token ? (int64_t)row_token[r] : r;
+      sv = scales[tk];
+      ro = (uint32_t)(r * ldo * ESZ);
+    }
+    s_rowoff[tid] = ro;
+    s_scale[tid] = sv;
+  }
   if (c.avalid) {
-    const int64_t r = r0 + m0 + tid;
+    const int64_t r = r0 + m0 + arow;
     atok = row_token ? (int64_t)row_token[r] : r;
-    s_scale[tid] = scales[atok];
-    s_rowoff[tid] = (uint32_t)(r * ldo * ESZ);
   }
   c.cres = make_rsrc(codes, 0x7FFFFFFFu);
   c.crow_off = (uint32_t)(atok * ((int64_t)K * ABITS / 8));
@@ -373,11 +379,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
     case 1: tile_run<BITS, ABITS, NW, 1, LT>(c, As, s_scale, s_rowoff, ores); break;
     case 2: tile_run<BITS, ABITS, NW, 2, LT>(c, As, s_scale, s_rowoff, ores); break;
     case 3: tile_run<BITS, ABITS, NW, 3, LT>(c, As, s_scale, s_rowoff, ores); break;
-    case 4: tile_run<BITS, ABITS, NW, 4, LT>(c, As, s_scale, s_rowoff, ores); break;
-    case 5: tile_run<BITS, ABITS, NW, 5, LT>(c, As, s_scale, s_rowoff, ores); break;
-    case 6: tile_run<BITS, ABITS, NW, 6, LT>(c, As, s_scale, s_rowoff, ores); break;
-    case 7: tile_run<BITS, ABITS, NW, 7, LT>(c, As, s_scale, s_rowoff, ores); break;
-    default: tile_run<BITS, ABITS, NW, 8, LT>(c, As, s_scale, s_rowoff, ores); break;
+    default: tile_run<BITS, ABITS, NW, 4, LT>(c, As, s_scale, s_rowoff, ores); break;
   }
 }
 
@@ -389,7 +391,7 @@ static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) 
   // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them
   const int64_t big = a.offsets ? std::min<int64_t>(E, a.n_rows / (min_rows + 1)) : 0;
   int64_t mtiles = (a.n_rows + BM - 1) / BM + big;
-  mtiles = (mtiles + 15) / 16 * 16;                  // a multiple of 16 (XCD pairs)
+  mtiles = (mtiles + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG M-tiles on each XCD
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT>), grid, dim3(256), 0, stream, a.codes,
