@@ -30,7 +30,7 @@ namespace cbq {
 
 namespace {
 constexpr int BM = 128;     // rows per tile (two threads convert each row's codes)
-constexpr int XG = 2;       // consecutive M-tiles kept on one XCD
+constexpr int XG = 4;       // consecutive M-tiles kept on one XCD
 constexpr int BK = 64;      // channels per step
 constexpr int LDW = BK + 8; // fp16 per LDS row (padding staggers the banks)
 
