@@ -10,17 +10,19 @@
 // the four waves.  Products are exact (int codes x fp16 centroids); only the fp32
 // summation order differs from the plain definition.
 //
-// Tile: up to 128 rows of one expert x 256 columns x 64 channels per step, four waves.
+// Tile: up to BM rows of one expert x 256 columns x 64 channels per step, four waves.
 // Wave w owns 64 columns (for the gate/up pair: 32 gate rows and the same 32 up rows,
 // so the SwiGLU epilogue finds g and u in one lane) and all rows of the tile, held as
-// up to 4 x 2 accumulators of 32x32 (128 registers); with 256 registers a wave, two
-// workgroups share each CU (two waves per SIMD), so one workgroup's epilogue, prologue
-// and waits overlap the other's MFMAs.  Only the 32-row sub-tiles that hold rows are
-// computed, so an expert's last tile wastes fewer than 32 rows.  A is double-buffered
-// in LDS (two threads convert each row's codes) and the next step's loads are issued
-// before this step's MFMAs.
+// up to BM/32 x 2 accumulators of 32x32.  For 2- and 3-bit codebooks BM = 128: 128
+// accumulator registers, 256 registers a wave, so two workgroups share each CU (two
+// waves per SIMD) and one workgroup's epilogue, prologue and waits overlap the other's
+// MFMAs.  For 4-bit codebooks, whose dequantisation is the heaviest vector work, BM =
+// 256 spreads each dequantised weight over twice the rows (one workgroup a CU).  Only
+// the 32-row sub-tiles that hold rows are computed, so an expert's last tile wastes
+// fewer than 32 rows.  A is double-buffered in LDS (converted by one or two threads per
+// row) and the next step's loads are issued before this step's MFMAs.
 //
-// A tile is one column range x the y-th 128-row slice in expert order, skipping
+// A tile is one column range x the y-th BM-row slice in expert order, skipping
 // experts with at most min_rows rows (those go to the decode path).
 #include <algorithm>
 
@@ -29,7 +31,11 @@
 namespace cbq {
 
 namespace {
-constexpr int BM = 128;     // rows per tile (two threads convert each row's codes)
+// Rows per tile: 256 (one thread per row, one workgroup a CU) for 4-bit codebooks, whose
+// dequantisation is the heaviest vector work and is best spread over the most rows;
+// 128 (two threads per row, two workgroups a CU) for 2- and 3-bit codebooks.
+template <int BITS>
+constexpr int tile_rows() { return BITS == 4 ? 256 : 128; }
 constexpr int XG = 4;       // consecutive M-tiles kept on one XCD
 constexpr int BK = 64;      // channels per step
 constexpr int LDW = BK + 8; // fp16 per LDS row (padding staggers the banks)
@@ -55,11 +61,13 @@ struct TileCtx {
   int K, g, nl, tid, rows;
 };
 
-template <int BITS, int ABITS, int NW, int NMS, bool LT>
+template <int BITS, int ABITS, int NW, int NMS, bool LT, int BM>
 __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint16_t (*As)[BM * LDW],
                                          const float* s_scale, const uint32_t* s_rowoff,
                                          __amdgpu_buffer_rsrc_t ores) {
   const int K = c.K, g = c.g, nl = c.nl, tid = c.tid;
+  constexpr int TPR = 256 / BM;            // threads per tile row (1 or 2)
+  constexpr int NPA = 8 / TPR;             // activation pieces per thread and step
   f32x16 acc[NMS][2];
 #pragma unroll
   for (int i = 0; i < NMS; ++i)
@@ -71,7 +79,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   // Raw loads run two steps ahead in a ring of two slots; the step loop is unrolled
   // by two so every slot index is a compile-time constant.
   uint32_t rw[2][2][BITS];     // [slot][matrix] raw indices
-  uint32_t ra[2][ABITS];       // [slot] raw activation codes (this thread's half row)
+  uint32_t ra[2][ABITS * 2 / TPR];   // [slot] raw activation codes (this thread's part of its row)
   uint32_t bdA[2][16], bdB[2][16];  // dequantised weights, alternating between steps
   f16x8 af[NMS];               // A fragments of the current 16-channel sub-step
 
@@ -82,19 +90,25 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       buf_load<4 * BITS>(c.wres[s], (c.nvalid[s] && kok) ? c.wrow_off[s] + (uint32_t)kt * c.wstep : kOffNone, w[s]);
-    const int ka = kt * BK + 32 * (tid & 1);
-    const bool okh = live && c.avalid && ka < K;
-    const uint32_t ab = c.crow_off + (uint32_t)(ka * ABITS / 8);
 #pragma unroll
-    for (int i = 0; i < ABITS / 4; ++i)       // this thread's 32 codes
-      buf_load<16>(c.cres, okh ? ab + 16 * i : kOffNone, a + 4 * i);
+    for (int hh = 0; hh < 2 / TPR; ++hh) {    // this thread's 32-code halves of the step
+      const int ka = kt * BK + 32 * ((tid % TPR) + hh);
+      const bool okh = live && c.avalid && ka < K;
+      const uint32_t ab = c.crow_off + (uint32_t)(ka * ABITS / 8);
+#pragma unroll
+      for (int i = 0; i < ABITS / 4; ++i)
+        buf_load<16>(c.cres, okh ? ab + 16 * i : kOffNone, a + ABITS * hh + 4 * i);
+    }
   };
   auto astore = [&](int buf, const uint32_t* a) {
     uint32_t d[16];
-    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][(tid >> 1) * LDW]) + 4 * (tid & 1);
-    codes32_to_f16_ord<ABITS, LT>(a, d);
+    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][(tid / TPR) * LDW]) + 4 * (tid % TPR);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ap[j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+    for (int h = 0; h < 2 / TPR; ++h) {
+      codes32_to_f16_ord<ABITS, LT>(a + h * ABITS, d);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ap[h * 4 + j] = u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]};
+    }
   };
   auto frag = [&](int buf, int kk, int ms) {
     return *reinterpret_cast<const f16x8*>(&As[buf][(ms * 32 + nl) * LDW + g * 32 + kk * 8]);
@@ -123,18 +137,18 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
       for (int i = 0; i < 4; ++i) d[4 * j + i] = tmp[4 * (j & 1) + i];
     }
   };
-  // Piece p (0..3) of this thread's half-row conversion: codes 8p..8p+7 of its 32 -> one
-  // 16-byte LDS store.
+  // Piece p (0 .. NPA-1) of this thread's conversion: codes 8p..8p+7 of its 64 / TPR ->
+  // one 16-byte LDS store.
   auto a_piece = [&](int buf, const uint32_t* a, int p) {
     uint32_t d[4];
-    codes8_group<ABITS, LT>(a, p, d);
-    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][(tid >> 1) * LDW]) + 4 * (tid & 1);
+    codes8_group<ABITS, LT>(a + (p >> 2) * ABITS, p & 3, d);
+    u32x4* ap = reinterpret_cast<u32x4*>(&As[buf][(tid / TPR) * LDW]) + 4 * (tid % TPR);
     ap[p] = u32x4{d[0], d[1], d[2], d[3]};
   };
   // One step: MFMAs on LDS buffer `buf` with weights `bd`, while step kt+1 is
   // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
-  // (wf, af_raw) is refilled with step kt+2.  The preparation is cut into 8 pieces (4 of
-  // activation conversion, 4 of the first matrix's dequantisation) placed between the
+  // (wf, af_raw) is refilled with step kt+2.  The preparation is cut into NPA + 4 pieces
+  // (activation conversion, then the first matrix's dequantisation) placed between the
   // MFMA pairs in program order (scheduling fences keep them there), so the vector ALU
   // work issues while the matrix cores are busy.
   auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
@@ -152,10 +166,11 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
         acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
         af[ms] = frag(buf, kk + 1, ms);
         const int i = kk * NMS + ms;
+        constexpr int NP = NPA + 4;
 #pragma unroll
-        for (int p = (8 * i + PRE - 1) / PRE; p < (8 * (i + 1) + PRE - 1) / PRE; ++p) {
-          if (p < 4) a_piece(buf ^ 1, an, p);
-          else dq_piece(0, wn[0], bn[0], p - 4);
+        for (int p = (NP * i + PRE - 1) / PRE; p < (NP * (i + 1) + PRE - 1) / PRE; ++p) {
+          if (p < NPA) a_piece(buf ^ 1, an, p);
+          else dq_piece(0, wn[0], bn[0], p - NPA);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -241,8 +256,8 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   }
 }
 
-template <int BITS, int ABITS, int NW, bool LT>
-__global__ void __launch_bounds__(256, 2)
+template <int BITS, int ABITS, int NW, bool LT, int BM = tile_rows<BITS>()>
+__global__ void __launch_bounds__(256, 256 / BM)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
@@ -253,7 +268,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDW];
   __shared__ __attribute__((aligned(16))) float s_scale[BM];
   __shared__ __attribute__((aligned(16))) uint32_t s_rowoff[BM];   // byte offset of each row in out
-  __shared__ int64_t s_r0, s_me, s_m0;
+  __shared__ int64_t s_r0, s_me, s_m0, s_ttot;
   __shared__ int s_e;
 
   const int tid = threadIdx.x;
@@ -261,14 +276,37 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so XCD x
   // gets ids x, x + 8, ...; those ids work through rounds of gridDim.x column tiles
   // of one M-tile each, so the column tiles of an M-tile (same activation rows) share
-  // one L2.  Rounds XG*P .. XG*P + XG - 1 of XCD x take the M-tiles XG*s .. XG*s + XG - 1,
-  // s = 8P + (x + P) % 8: runs of XG consecutive M-tiles (mostly of one expert: the same
-  // weights) stay on one XCD, and the slot rotates with P to spread the work.  (The host
-  // makes the M-tile slots a multiple of 8 * XG.)
+  // one L2.  Rounds G*P .. G*P + G - 1 of XCD x take the M-tiles G*(8P + x) .. + G - 1:
+  // runs of G consecutive M-tiles (mostly of one expert: the same weights) stay on one
+  // XCD.  G is the largest power of two <= XG with 8G <= T, the call's M-tile count
+  // (counted first), so a call of few tiles still spreads them over all eight XCDs.
+  // (The host makes the M-tile slots a multiple of 8 * XG, XG a power of two, so the
+  // slots map one to one onto M-tiles 0 .. slots - 1.)
+  if (tid < 64) {
+    int64_t tot = 0;
+    if (!offsets) {
+      tot = n_rows > min_rows ? (n_rows + BM - 1) / BM : 0;
+    } else {
+      for (int base = 0; base < E; base += 64) {
+        const int ex = base + tid;
+        int64_t cnt = 0;
+        if (ex < E) cnt = offsets[ex + 1] - offsets[ex];
+        int64_t nt = cnt > min_rows ? (cnt + BM - 1) / BM : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) nt += __shfl_xor(nt, d);
+        tot += nt;
+      }
+    }
+    if (tid == 0) s_ttot = tot;
+  }
+  __syncthreads();
+  const int64_t ttot = s_ttot;
+  uint32_t G = 1;                                    // a power of two, so it divides the
+  while (2 * G <= XG && 8 * 2 * G <= ttot) G *= 2;   // rounds per XCD (a multiple of XG)
   const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
   const uint32_t q = (lin / 8) / gridDim.x;
-  const uint32_t P = q / XG;
-  const int64_t ty = XG * (8 * (int64_t)P + (lin % 8 + P) % 8) + (q % XG);
+  const uint32_t P = q / G;
+  const int64_t ty = (int64_t)G * (8 * (int64_t)P + lin % 8) + (q % G);
   const int tcol = (int)((lin / 8) % gridDim.x);
   // ---- M-tile -> (expert, first row): wave 0 scans the experts' tile counts ----
   if (tid < 64) {
@@ -312,7 +350,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   c.tid = tid;
   c.rows = rows;
   // ---- activation loader: threads 2i and 2i + 1 own the two 32-code halves of tile row i ----
-  const int arow = tid >> 1;                         // two threads per tile row
+  const int arow = tid / (256 / BM);                 // one or two threads per tile row
   c.avalid = arow < rows;
   int64_t atok = 0;
   constexpr uint32_t ESZ = NW == 2 ? 2 : 4;
@@ -376,15 +414,26 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // output buffer: every row of this call (n_rows) x ldo elements
   const __amdgpu_buffer_rsrc_t ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
   switch (nms) {
-    case 1: tile_run<BITS, ABITS, NW, 1, LT>(c, As, s_scale, s_rowoff, ores); break;
-    case 2: tile_run<BITS, ABITS, NW, 2, LT>(c, As, s_scale, s_rowoff, ores); break;
-    case 3: tile_run<BITS, ABITS, NW, 3, LT>(c, As, s_scale, s_rowoff, ores); break;
-    default: tile_run<BITS, ABITS, NW, 4, LT>(c, As, s_scale, s_rowoff, ores); break;
+    case 1: tile_run<BITS, ABITS, NW, 1, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 2: tile_run<BITS, ABITS, NW, 2, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 3: tile_run<BITS, ABITS, NW, 3, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 4: tile_run<BITS, ABITS, NW, 4, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+    default:
+      if constexpr (BM == 256) {
+        switch (nms) {
+          case 5: tile_run<BITS, ABITS, NW, 5, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+          case 6: tile_run<BITS, ABITS, NW, 6, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+          case 7: tile_run<BITS, ABITS, NW, 7, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+          default: tile_run<BITS, ABITS, NW, 8, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+        }
+      }
+      break;
   }
 }
 
 template <int BITS, int ABITS, bool LT>
 static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
+  constexpr int BM = tile_rows<BITS>();
   const int E = a.offsets ? a.E : 1;
   const int ncol = a.n_w == 2 ? 128 : 256;
   // M-tile slots: an expert of r rows takes ceil(r / BM) <= r / BM + 1 of them, and only
