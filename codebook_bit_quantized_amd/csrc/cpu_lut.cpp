@@ -11,12 +11,17 @@
 //
 // Index unpacking: 4-bit nibbles with byte shuffles; 3- and 2-bit fields with BMI2
 // pdep (eight indices per 24 or 16 bits).  On CPUs with AVX-512 a second variant
-// looks 16 weights up per vpermps in an fp32 copy of the row's codebook.
+// looks 16 weights up per vpermps in an fp32 copy of the row's codebook and computes
+// 4 rows x up to 4 tokens per pass.  Rows are split over a persistent thread pool.
 #include "cpu_lut.hpp"
 
 #include <immintrin.h>
+#include <unistd.h>
 
 #include <algorithm>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -125,13 +130,13 @@ void rows_kernel(const float* a, const float* scales, int64_t T, int64_t n0, int
   }
 }
 
-// AVX-512 variant: the codebook is widened once per row into an fp32 table of 16
-// lanes, and vpermps looks up 16 weights per instruction, already as fp32.  Indices
-// are spread into bytes with pdep, then zero-extended to 16 dwords.
+// AVX-512 variant: each row's codebook is widened once into an fp32 table of 16 lanes,
+// and vpermps looks up 16 weights per instruction, already as fp32.  A micro-kernel takes
+// 4 rows x TB tokens: per 32 channels, 8 lookups and 2 TB activation loads feed 8 TB FMAs,
+// so every activation load serves four rows.
 template <int BITS>
 __attribute__((target("avx512f,bmi2"))) inline __m512i load_indices16(const uint8_t* row, int k) {
-  constexpr uint64_t MASK = BITS == 4 ? 0x0F0F0F0F0F0F0F0Full
-                          : BITS == 3 ? 0x0707070707070707ull : 0x0303030303030303ull;
+  constexpr uint64_t MASK = BITS == 3 ? 0x0707070707070707ull : 0x0303030303030303ull;
   constexpr int GB = BITS;                                  // bytes per 8 indices
   const uint8_t* p = row + (int64_t)k * BITS / 8;
   uint64_t f0 = 0, f1 = 0;
@@ -143,34 +148,65 @@ __attribute__((target("avx512f,bmi2"))) inline __m512i load_indices16(const uint
   return _mm512_cvtepu8_epi32(bytes);
 }
 
-// TB <= 16 tokens: their accumulators fit the 32 vector registers with the weights.
+// Indices k .. k+31 of a row as two vectors of 16 dwords.
+template <int BITS>
+__attribute__((target("avx512f,bmi2"))) inline void load_indices32(const uint8_t* row, int k,
+                                                                   __m512i& i0, __m512i& i1) {
+  if constexpr (BITS == 4) {
+    const __m128i p = _mm_loadu_si128(reinterpret_cast<const __m128i*>(row + k / 2));
+    const __m128i m = _mm_set1_epi8(0x0F);
+    const __m128i lo = _mm_and_si128(p, m);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(p, 4), m);
+    i0 = _mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi));
+    i1 = _mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi));
+  } else {
+    i0 = load_indices16<BITS>(row, k);
+    i1 = load_indices16<BITS>(row, k + 16);
+  }
+}
+
+// Rows n .. n+3 against tokens t0 .. t0+TB-1.  One token keeps two partial sums per row
+// (the 16-channel halves) so the FMA latency never limits the loop; more tokens keep one.
 template <int BITS, int TB>
 __attribute__((target("avx512f,bmi2")))
-inline void row_tokens512(const float* a, const float* scales, int64_t t0, int K, const uint8_t* row,
-                          __m512 tab, float* out, int64_t ldo, int64_t n) {
-  constexpr int NA = TB <= 2 ? 4 : (TB <= 4 ? 2 : 1);
-  __m512 acc[TB][NA];
-#pragma GCC unroll 16
-  for (int t = 0; t < TB; ++t)
+inline void block512(const float* a, const float* scales, int64_t t0, int K, const uint8_t* row0,
+                     int64_t row_bytes, const __m512* tab, float* out, int64_t ldo, int64_t n) {
+  constexpr int NA = TB == 1 ? 2 : 1;
+  __m512 acc[4][TB][NA];
 #pragma GCC unroll 4
-    for (int q = 0; q < NA; ++q) acc[t][q] = _mm512_setzero_ps();
+  for (int r = 0; r < 4; ++r)
+#pragma GCC unroll 4
+    for (int t = 0; t < TB; ++t)
+#pragma GCC unroll 2
+      for (int q = 0; q < NA; ++q) acc[r][t][q] = _mm512_setzero_ps();
   for (int k = 0; k < K; k += 32) {
-    const __m512 w0 = _mm512_permutexvar_ps(load_indices16<BITS>(row, k), tab);
-    const __m512 w1 = _mm512_permutexvar_ps(load_indices16<BITS>(row, k + 16), tab);
-#pragma GCC unroll 16
+    __m512 w0[4], w1[4];
+#pragma GCC unroll 4
+    for (int r = 0; r < 4; ++r) {
+      __m512i i0, i1;
+      load_indices32<BITS>(row0 + r * row_bytes, k, i0, i1);
+      w0[r] = _mm512_permutexvar_ps(i0, tab[r]);
+      w1[r] = _mm512_permutexvar_ps(i1, tab[r]);
+    }
+#pragma GCC unroll 4
     for (int t = 0; t < TB; ++t) {
       const float* at = a + (t0 + t) * (int64_t)K + k;
-      acc[t][0] = _mm512_fmadd_ps(w0, _mm512_loadu_ps(at), acc[t][0]);
-      acc[t][1 % NA] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(at + 16), acc[t][1 % NA]);
+      const __m512 a0 = _mm512_loadu_ps(at);
+#pragma GCC unroll 4
+      for (int r = 0; r < 4; ++r) acc[r][t][0] = _mm512_fmadd_ps(w0[r], a0, acc[r][t][0]);
+      const __m512 a1 = _mm512_loadu_ps(at + 16);
+#pragma GCC unroll 4
+      for (int r = 0; r < 4; ++r) acc[r][t][NA - 1] = _mm512_fmadd_ps(w1[r], a1, acc[r][t][NA - 1]);
     }
   }
-#pragma GCC unroll 16
-  for (int t = 0; t < TB; ++t) {
-    __m512 v = acc[t][0];
 #pragma GCC unroll 4
-    for (int q = 1; q < NA; ++q) v = _mm512_add_ps(v, acc[t][q]);
-    out[(t0 + t) * ldo + n] = scales[t0 + t] * _mm512_reduce_add_ps(v);
-  }
+  for (int r = 0; r < 4; ++r)
+#pragma GCC unroll 4
+    for (int t = 0; t < TB; ++t) {
+      __m512 v = acc[r][t][0];
+      if constexpr (NA == 2) v = _mm512_add_ps(v, acc[r][t][1]);
+      out[(t0 + t) * ldo + n + r] = scales[t0 + t] * _mm512_reduce_add_ps(v);
+    }
 }
 
 template <int BITS>
@@ -179,33 +215,95 @@ void rows_kernel512(const float* a, const float* scales, int64_t T, int64_t n0, 
                     const uint8_t* idx, const uint16_t* codebook, float* out, int64_t ldo) {
   constexpr int L = 1 << BITS;
   const int64_t row_bytes = (int64_t)K * BITS / 8;
-  for (int64_t n = n0; n < n1; ++n) {
-    alignas(64) float ctab[16] = {0};
-    for (int c = 0; c < L; ++c) ctab[c] = _cvtsh_ss(codebook[n * L + c]);
-    const __m512 tab = _mm512_load_ps(ctab);
-    const uint8_t* row = idx + n * row_bytes;
+  for (int64_t n = n0; n < n1; n += 4) {               // n1 - n0 is a multiple of 4
+    __m512 tab[4];
+    for (int r = 0; r < 4; ++r) {
+      alignas(64) float ctab[16] = {0};
+      for (int c = 0; c < L; ++c) ctab[c] = _cvtsh_ss(codebook[(n + r) * L + c]);
+      tab[r] = _mm512_load_ps(ctab);
+    }
+    const uint8_t* row0 = idx + n * row_bytes;
     int64_t t0 = 0;
-    for (; t0 + 16 <= T; t0 += 16) row_tokens512<BITS, 16>(a, scales, t0, K, row, tab, out, ldo, n);
+    for (; t0 + 4 <= T; t0 += 4) block512<BITS, 4>(a, scales, t0, K, row0, row_bytes, tab, out, ldo, n);
     switch (T - t0) {
-      case 1: row_tokens512<BITS, 1>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 2: row_tokens512<BITS, 2>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 3: row_tokens512<BITS, 3>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 4: row_tokens512<BITS, 4>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 5: row_tokens512<BITS, 5>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 6: row_tokens512<BITS, 6>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 7: row_tokens512<BITS, 7>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 8: row_tokens512<BITS, 8>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 9: row_tokens512<BITS, 9>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 10: row_tokens512<BITS, 10>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 11: row_tokens512<BITS, 11>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 12: row_tokens512<BITS, 12>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 13: row_tokens512<BITS, 13>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 14: row_tokens512<BITS, 14>(a, scales, t0, K, row, tab, out, ldo, n); break;
-      case 15: row_tokens512<BITS, 15>(a, scales, t0, K, row, tab, out, ldo, n); break;
+      case 1: block512<BITS, 1>(a, scales, t0, K, row0, row_bytes, tab, out, ldo, n); break;
+      case 2: block512<BITS, 2>(a, scales, t0, K, row0, row_bytes, tab, out, ldo, n); break;
+      case 3: block512<BITS, 3>(a, scales, t0, K, row0, row_bytes, tab, out, ldo, n); break;
       default: break;
     }
   }
 }
+
+// A fixed set of worker threads, started on the first multi-threaded call and kept for
+// the life of the process: a call hands each worker one range of rows and waits.
+class Pool {
+ public:
+  static Pool& get() {
+    static Pool p;
+    return p;
+  }
+  int size() const { return (int)workers_.size() + 1; }
+  // The pool's threads exist only in the process that started them (not after a fork).
+  bool usable() const { return pid_ == getpid(); }
+  // Runs job(0) .. job(n - 1), n <= size(), job(0) on the calling thread.
+  void run(int n, const std::function<void(int)>& job) {
+    std::unique_lock<std::mutex> call(call_mu_);        // one call at a time
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      job_ = &job;
+      n_ = n;
+      pending_ = n - 1;
+      ++gen_;
+    }
+    cv_.notify_all();
+    job(0);
+    std::unique_lock<std::mutex> lk(mu_);
+    done_.wait(lk, [&] { return pending_ == 0; });
+    job_ = nullptr;
+  }
+
+ private:
+  Pool() : pid_(getpid()) {
+    const int hw = (int)std::max(1u, std::thread::hardware_concurrency());
+    for (int i = 1; i < hw; ++i) workers_.emplace_back([this, i] { loop(i); });
+  }
+  ~Pool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& w : workers_) w.join();
+  }
+  void loop(int i) {
+    uint64_t seen = 0;
+    for (;;) {
+      const std::function<void(int)>* job;
+      int n;
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+        job = job_;
+        n = n_;
+      }
+      if (i < n) {
+        (*job)(i);
+        std::lock_guard<std::mutex> lk(mu_);
+        if (--pending_ == 0) done_.notify_one();
+      }
+    }
+  }
+  pid_t pid_;
+  std::vector<std::thread> workers_;
+  std::mutex mu_, call_mu_;
+  std::condition_variable cv_, done_;
+  const std::function<void(int)>* job_ = nullptr;
+  int n_ = 0, pending_ = 0;
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
 
 }  // namespace
 
@@ -250,13 +348,21 @@ void cpu_lut_gemm_impl(const uint8_t* codes, const float* scales, int act_bits, 
     run(0, N);
     return;
   }
-  std::vector<std::thread> pool;
-  const int64_t per = (N + nt - 1) / nt;
-  for (int i = 0; i < nt; ++i) {
+  Pool& pool = Pool::get();
+  if (pool.usable()) nt = std::min(nt, pool.size());
+  const int64_t per = ((N + nt - 1) / nt + 3) / 4 * 4;   // whole 4-row blocks per thread
+  auto part = [&](int i) {
     const int64_t n0 = i * per, n1 = std::min<int64_t>(N, n0 + per);
-    if (n0 < n1) pool.emplace_back(run, n0, n1);
+    if (n0 < n1) run(n0, n1);
+  };
+  if (pool.usable()) {
+    pool.run(nt, part);
+    return;
   }
-  for (auto& th : pool) th.join();
+  std::vector<std::thread> threads;                       // a forked child: plain threads
+  for (int i = 1; i < nt; ++i) threads.emplace_back(part, i);
+  part(0);
+  for (auto& th : threads) th.join();
 }
 
 }  // namespace cbq
