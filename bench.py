@@ -855,9 +855,9 @@ def main():
                     help="index layout the GEMMs read: regrouped by cbq_prepack_weights "
                          "(default) or the row bitstreams as generated")
     ap.add_argument("--tables", choices=("default", "lds", "reg"), default="default",
-                    help="where 2- and 3-bit codebooks are looked up: each path's default (LDS "
-                         "pair tables for the LUT path, register tables for the MFMA path), or "
-                         "forced for every GEMM")
+                    help="where 2- and 3-bit codebooks are looked up: the library's default (LUT "
+                         "path: LDS pair tables, except register tables for 3-bit blocked "
+                         "weights; MFMA path: register tables), or forced for every GEMM")
     ap.add_argument("--dense-rotation", action="store_true",
                     help="measure the dense K x K rotation variant of rotate_quantize instead")
     ap.add_argument("--decode-overlap", choices=("down", "serial"), default="down",

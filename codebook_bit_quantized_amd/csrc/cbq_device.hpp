@@ -121,11 +121,38 @@ __device__ __forceinline__ void dequant2(const RowTable<2>& t, uint32_t x, uint3
 #undef CBQ_SEL2
 }
 
+// 3-bit units of the blocked layout (cbq_prepack_weights).  Group g < 3 (indices
+// 8g .. 8g+7 of the unit) is dword g: byte b holds index 8g+2b in bits 0-2 and 8g+2b+1 in
+// bits 3-5.  Group 3's six-bit pairs are spread over the spare top bits: pair b's bits
+// 2i .. 2i+1 are bits 6-7 of byte b of dword i.  This gathers group 3 into the same form.
+__device__ __forceinline__ uint32_t group3_blk(const uint32_t* w) {
+  return ((w[0] >> 6) & 0x03030303u) | ((w[1] >> 4) & 0x0C0C0C0Cu) | ((w[2] >> 2) & 0x30303030u);
+}
+
+// 3-bit, one group in the blocked form (only bits 0-5 of each byte are read) -> D0..D3:
+// the even indices' and the odd indices' selectors are one mask and one shift-and-mask.
+__device__ __forceinline__ void dequant3_blk(const RowTable<3>& t, uint32_t x, uint32_t* d) {
+  const uint32_t se = x & 0x07070707u;                 // bytes i0 i2 i4 i6
+  const uint32_t so = (x >> 3) & 0x07070707u;          // bytes i1 i3 i5 i7
+  const uint32_t le = perm(t.lo[1], t.lo[0], se), he = perm(t.hi[1], t.hi[0], se);
+  const uint32_t lo = perm(t.lo[1], t.lo[0], so), ho = perm(t.hi[1], t.hi[0], so);
+  d[0] = perm(he, le, 0x05010400u);   // (k0, k2)
+  d[1] = perm(he, le, 0x07030602u);   // (k4, k6)
+  d[2] = perm(ho, lo, 0x05010400u);   // (k1, k3)
+  d[3] = perm(ho, lo, 0x07030602u);   // (k5, k7)
+}
+
 // Dequantise 32 consecutive indices (one lane's slice: 4*BITS bytes already loaded
-// into w[0..BITS-1]) into 16 dwords: group j (indices 8j..8j+7) -> d[4j..4j+3].
-template <int BITS>
+// into w[0..BITS-1]) into 16 dwords: group j (indices 8j..8j+7) -> d[4j..4j+3].  BLK:
+// the slice is a unit of the blocked layout (which re-encodes 3-bit units).
+template <int BITS, bool BLK = false>
 __device__ __forceinline__ void dequant32(const RowTable<BITS>& t, const uint32_t* w, uint32_t* d) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 3 && BLK) {
+    dequant3_blk(t, w[0], d + 0);
+    dequant3_blk(t, w[1], d + 4);
+    dequant3_blk(t, w[2], d + 8);
+    dequant3_blk(t, group3_blk(w), d + 12);
+  } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) dequant4(t, w[j], d + 4 * j);
   } else if constexpr (BITS == 3) {
@@ -244,19 +271,26 @@ __device__ __forceinline__ uint32_t pair_field(const uint32_t* w, int j) {
 }
 
 // Pairs 4p .. 4p+3 of the lane's 32 indices -> d[0..3], from the table row whose entry 0
-// is dword `row` of `tab` (entries R dwords apart).
-template <int BITS, int R>
+// is dword `row` of `tab` (entries R dwords apart).  BLK: a 3-bit unit of the blocked
+// layout, whose pair 4p + b is bits 0-5 of byte b of group p.
+template <int BITS, int R, bool BLK = false>
 __device__ __forceinline__ void pair_lookup8(const uint32_t* tab, uint32_t row, const uint32_t* w,
                                              int p, uint32_t* d) {
+  if constexpr (BITS == 3 && BLK) {
+    const uint32_t x = p < 3 ? w[p] : group3_blk(w);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = tab[row + pair_field<BITS>(w, 4 * p + q) * R];
+    for (int q = 0; q < 4; ++q) d[q] = tab[row + __builtin_amdgcn_ubfe(x, 8u * q, 6u) * R];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = tab[row + pair_field<BITS>(w, 4 * p + q) * R];
+  }
 }
 
-template <int BITS, int R>
+template <int BITS, int R, bool BLK = false>
 __device__ __forceinline__ void pair_lookup32(const uint32_t* tab, uint32_t row, const uint32_t* w,
                                               uint32_t* d) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) pair_lookup8<BITS, R>(tab, row, w, p, d + 4 * p);
+  for (int p = 0; p < 4; ++p) pair_lookup8<BITS, R, BLK>(tab, row, w, p, d + 4 * p);
 }
 
 // This lane's share of one row's table: P lanes (sub = 0 .. P-1) build the row, lane sub

@@ -52,7 +52,8 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, bool ok, uint32_t* 
 
 // LT: weights looked up in LDS pair tables (2- and 3-bit codebooks), shared by the
 // workgroup's waves (they serve the same rows); otherwise in per-row register tables.
-template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH>
+// BLK: 3-bit indices in the blocked layout's re-encoded units (cbq_prepack_weights).
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH, bool BLK>
 __global__ void __launch_bounds__(NW == 2 ? 512 : 1024, BITS <= 3 ? 4 : 3)
 lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
@@ -187,8 +188,8 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
         uint32_t bd[NW][16];
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          if constexpr (LT) pair_lookup32<BITS, 16>(ptab, trow[0][w], cur.w[0][w], bd[w]);
-          else dequant32<BITS>(tab[0][w], cur.w[0][w], bd[w]);
+          if constexpr (LT) pair_lookup32<BITS, 16, BLK>(ptab, trow[0][w], cur.w[0][w], bd[w]);
+          else dequant32<BITS, BLK>(tab[0][w], cur.w[0][w], bd[w]);
         }
 #pragma unroll
         for (int s = 0; s < MSUB; ++s) {
@@ -216,8 +217,8 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
         uint32_t bd[NW][16];
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          if constexpr (LT) pair_lookup32<BITS, 16>(ptab, trow[q][w], cur.w[q][w], bd[w]);
-          else dequant32<BITS>(tab[q][w], cur.w[q][w], bd[w]);
+          if constexpr (LT) pair_lookup32<BITS, 16, BLK>(ptab, trow[q][w], cur.w[q][w], bd[w]);
+          else dequant32<BITS, BLK>(tab[q][w], cur.w[q][w], bd[w]);
         }
 #pragma unroll
         for (int s = 0; s < MSUB; ++s) {
@@ -300,16 +301,24 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
   }
 }
 
-template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH>
-static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH, bool BLK>
+static hipError_t launch_t2(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
   const int E = a.offsets ? a.E : 1;
   dim3 grid((unsigned)((a.N + 16 * NG - 1) / (16 * NG)), (unsigned)E);
   const size_t lds = (size_t)(splitk - 1) * NG * NW * MSUB * 64 * sizeof(f32x4) +
                      (LT ? (size_t)NG * NW * PairTab<BITS>::NE * 16 * sizeof(uint32_t) : 0);
-  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG, LT, DEPTH>), grid, dim3(64 * splitk), lds,
+  hipLaunchKernelGGL((lut_decode_kernel<BITS, ABITS, NW, MSUB, NG, LT, DEPTH, BLK>), grid, dim3(64 * splitk), lds,
                      stream, a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows,
                      a.N, a.K, splitk, max_rows, a.blocked, a.out, a.ldo);
   return hipGetLastError();
+}
+
+template <int BITS, int ABITS, int NW, int MSUB, int NG, bool LT, int DEPTH>
+static hipError_t launch_t(const GemmArgs& a, int max_rows, int splitk, hipStream_t stream) {
+  if constexpr (BITS == 3) {
+    if (a.blocked) return launch_t2<BITS, ABITS, NW, MSUB, NG, LT, DEPTH, true>(a, max_rows, splitk, stream);
+  }
+  return launch_t2<BITS, ABITS, NW, MSUB, NG, LT, DEPTH, false>(a, max_rows, splitk, stream);
 }
 
 // Row groups per wave: a single matrix with 2- or 3-bit tables (8 VGPRs per row)
@@ -334,13 +343,17 @@ static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStrea
                  : launch_t<BITS, ABITS, 1, 2, 1, LT, 2>(a, max_rows, splitk, s);
 }
 
-// 2- and 3-bit codebooks: LDS pair tables unless the register tables are asked for (the
-// lookups take fewer vector instructions, and the LDS tables measured slightly faster
-// here); 4-bit pair tables would take 256 entries a row, so 4-bit tables stay in registers
+// Where 2- and 3-bit codebooks are looked up by default, as measured on the decode GEMMs:
+// LDS pair tables (one lookup per two weights) for 2-bit codebooks and for 3-bit ones in
+// the row layout; register tables for 3-bit codebooks in the blocked layout, whose
+// re-encoded units make the register selectors one mask or one shift and a mask.  4-bit
+// pair tables would take 256 entries a row, so 4-bit tables stay in registers.
 template <int BITS, int ABITS>
 static hipError_t launch_b(const GemmArgs& a, int max_rows, int splitk, hipStream_t s) {
   if constexpr (BITS <= 3) {
-    if (a.tables != kTablesReg) return launch_b<BITS, ABITS, true>(a, max_rows, splitk, s);
+    const bool lds = a.tables == kTablesLds ||
+                     (a.tables == kTablesDefault && !(BITS == 3 && a.blocked));
+    if (lds) return launch_b<BITS, ABITS, true>(a, max_rows, splitk, s);
   }
   return launch_b<BITS, ABITS, false>(a, max_rows, splitk, s);
 }

@@ -61,7 +61,7 @@ struct TileCtx {
   int K, g, nl, tid, rows;
 };
 
-template <int BITS, int ABITS, int NW, int NMS, bool LT, int BM>
+template <int BITS, int ABITS, int NW, int NMS, bool LT, bool BLK, int BM>
 __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint16_t (*As)[BM * LDW],
                                          const float* s_scale, const uint32_t* s_rowoff,
                                          __amdgpu_buffer_rsrc_t ores) {
@@ -113,19 +113,15 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   auto frag = [&](int buf, int kk, int ms) {
     return *reinterpret_cast<const f16x8*>(&As[buf][(ms * 32 + nl) * LDW + g * 32 + kk * 8]);
   };
-  // One step: MFMAs on LDS buffer `buf` with weights `bd`, while step kt+1 is
-  // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
-  // (wf, af_raw) is refilled with step kt+2.  Sub-steps 0-2 run before the barrier
-  // (with the activation conversion and the first matrix's dequantisation); sub-step
-  // 3 runs after it from fragments already in registers, so the next step's first
-  // fragment reads (which need the barrier) overlap MFMAs instead of stalling.
   // Piece j (0..3) of one lane's 32-index dequantisation of matrix slot s: indices 8j..8j+7.
   auto dq_piece = [&](int s, const uint32_t (&w)[BITS], uint32_t* d, int j) {
     const RowTable<BITS>& t = c.tab[s];
     if constexpr (LT) {
-      pair_lookup8<BITS, 32>(c.ptab, c.trow[s], w, j, d + 4 * j);
+      pair_lookup8<BITS, 32, BLK>(c.ptab, c.trow[s], w, j, d + 4 * j);
     } else if constexpr (BITS == 4) {
       dequant4(t, w[j], d + 4 * j);
+    } else if constexpr (BITS == 3 && BLK) {
+      dequant3_blk(t, j < 3 ? w[j] : group3_blk(w), d + 4 * j);
     } else if constexpr (BITS == 3) {
       const uint32_t f = j == 0 ? w[0] : j == 1 ? __builtin_amdgcn_alignbit(w[1], w[0], 24)
                        : j == 2 ? __builtin_amdgcn_alignbit(w[2], w[1], 16) : (w[2] >> 8);
@@ -149,8 +145,11 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   // prepared from ring slot (wn, an) into `bn` and the other LDS buffer, and ring slot
   // (wf, af_raw) is refilled with step kt+2.  The preparation is cut into NPA + 4 pieces
   // (activation conversion, then the first matrix's dequantisation) placed between the
-  // MFMA pairs in program order (scheduling fences keep them there), so the vector ALU
-  // work issues while the matrix cores are busy.
+  // MFMA pairs of sub-steps 0-2 in program order (scheduling fences keep them there), so
+  // the vector ALU work issues while the matrix cores are busy.  Sub-step 3 runs after
+  // the barrier from fragments already in registers, beside the second matrix's
+  // dequantisation, so the next step's first fragment reads (which need the barrier)
+  // overlap MFMAs instead of stalling.
   auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
                   uint32_t (&wn)[2][BITS], uint32_t* an, uint32_t (&wf)[2][BITS], uint32_t* af_raw) {
     gload(kt + 2, wf, af_raw);
@@ -197,8 +196,8 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   astore(0, ra[0]);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    if constexpr (LT) pair_lookup32<BITS, 32>(c.ptab, c.trow[s], rw[0][s], bdA[s]);
-    else dequant32<BITS>(c.tab[s], rw[0][s], bdA[s]);
+    if constexpr (LT) pair_lookup32<BITS, 32, BLK>(c.ptab, c.trow[s], rw[0][s], bdA[s]);
+    else dequant32<BITS, BLK>(c.tab[s], rw[0][s], bdA[s]);
   }
   lds_barrier();
 #pragma unroll
@@ -256,7 +255,8 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   }
 }
 
-template <int BITS, int ABITS, int NW, bool LT, int BM = tile_rows<BITS>()>
+// BLK: 3-bit indices in the blocked layout's re-encoded units (cbq_prepack_weights).
+template <int BITS, int ABITS, int NW, bool LT, bool BLK, int BM = tile_rows<BITS>()>
 __global__ void __launch_bounds__(256, 256 / BM)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
@@ -414,25 +414,25 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // output buffer: every row of this call (n_rows) x ldo elements
   const __amdgpu_buffer_rsrc_t ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
   switch (nms) {
-    case 1: tile_run<BITS, ABITS, NW, 1, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
-    case 2: tile_run<BITS, ABITS, NW, 2, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
-    case 3: tile_run<BITS, ABITS, NW, 3, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
-    case 4: tile_run<BITS, ABITS, NW, 4, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 1: tile_run<BITS, ABITS, NW, 1, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 2: tile_run<BITS, ABITS, NW, 2, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 3: tile_run<BITS, ABITS, NW, 3, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 4: tile_run<BITS, ABITS, NW, 4, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
     default:
       if constexpr (BM == 256) {
         switch (nms) {
-          case 5: tile_run<BITS, ABITS, NW, 5, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
-          case 6: tile_run<BITS, ABITS, NW, 6, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
-          case 7: tile_run<BITS, ABITS, NW, 7, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
-          default: tile_run<BITS, ABITS, NW, 8, LT, BM>(c, As, s_scale, s_rowoff, ores); break;
+          case 5: tile_run<BITS, ABITS, NW, 5, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+          case 6: tile_run<BITS, ABITS, NW, 6, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+          case 7: tile_run<BITS, ABITS, NW, 7, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+          default: tile_run<BITS, ABITS, NW, 8, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
         }
       }
       break;
   }
 }
 
-template <int BITS, int ABITS, bool LT>
-static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
+template <int BITS, int ABITS, bool LT, bool BLK>
+static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream) {
   constexpr int BM = tile_rows<BITS>();
   const int E = a.offsets ? a.E : 1;
   const int ncol = a.n_w == 2 ? 128 : 256;
@@ -443,14 +443,23 @@ static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) 
   mtiles = (mtiles + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG M-tiles on each XCD
   dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
   if (a.n_w == 2)
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT>), grid, dim3(256), 0, stream, a.codes,
+    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK>), grid, dim3(256), 0, stream, a.codes,
                        a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
                        min_rows, a.blocked, a.out, a.ldo);
   else
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT>), grid, dim3(256), 0, stream, a.codes,
+    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK>), grid, dim3(256), 0, stream, a.codes,
                        a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
                        min_rows, a.blocked, a.out, a.ldo);
   return hipGetLastError();
+}
+
+// 3-bit weights in the blocked layout take the kernels for its re-encoded units.
+template <int BITS, int ABITS, bool LT>
+static hipError_t launch_p(const GemmArgs& a, int min_rows, hipStream_t stream) {
+  if constexpr (BITS == 3) {
+    if (a.blocked) return launch_p2<BITS, ABITS, LT, true>(a, min_rows, stream);
+  }
+  return launch_p2<BITS, ABITS, LT, false>(a, min_rows, stream);
 }
 
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream) {

@@ -2,9 +2,13 @@
 // every 16-row x 128-channel tile of a weight matrix in 256*bits contiguous bytes, in the
 // order the GEMM waves load them (lane 16j + r holds row r's indices of channels
 // 32j .. 32j+31 of the chunk), so a wave's index load is one coalesced block instead of
-// sixteen short pieces of sixteen rows.  Each unit copied is the 4*bits bytes of 32
-// consecutive indices of one row, byte-aligned in both layouts (K % 32 == 0), so the
-// regrouping moves whole dwords and never touches the bit order.
+// sixteen short pieces of sixteen rows.  Each unit is the 4*bits bytes of 32
+// consecutive indices of one row, byte-aligned in both layouts (K % 32 == 0).  2- and
+// 4-bit units are copied as they are.  3-bit units are re-encoded so the kernels build
+// their byte selectors with one mask or one shift and a mask: group g < 3 (indices
+// 8g .. 8g+7) becomes dword g, byte b holding index 8g+2b in bits 0-2 and 8g+2b+1 in
+// bits 3-5; group 3's pair b (i_{24+2b} | i_{25+2b} << 3) is spread over bits 6-7 of
+// byte b of the three dwords, two bits each, lowest first.
 #include "cbq_internal.hpp"
 
 namespace cbq {
@@ -33,6 +37,28 @@ prepack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64
   } else {
 #pragma unroll
     for (int i = 0; i < BITS; ++i) w[i] = 0u;    // channels past K: index 0, never used
+  }
+  if constexpr (BITS == 3) {
+    // index k of the LSB-first unit: bits 3k .. 3k+2 of w[0] | w[1] << 32 | w[2] << 64
+    auto idx = [&](int k) -> uint32_t {
+      const int bit = 3 * k, wi = bit >> 5, sh = bit & 31;
+      const uint32_t lo = w[wi] >> sh;
+      const uint32_t hi = (sh > 29 && wi < 2) ? (w[wi + 1] << (32 - sh)) : 0u;
+      return (lo | hi) & 7u;
+    };
+    uint32_t o[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < 3; ++g)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[g] |= (idx(8 * g + 2 * b) | (idx(8 * g + 2 * b + 1) << 3)) << (8 * b);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t pr = idx(24 + 2 * b) | (idx(25 + 2 * b) << 3);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) o[i] |= ((pr >> (2 * i)) & 3u) << (8 * b + 6);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) w[i] = o[i];
   }
   uint32_t* d = reinterpret_cast<uint32_t*>(dst + u * 4 * BITS);
 #pragma unroll

@@ -72,9 +72,11 @@ enum {
 
 /* Flags added to a path to choose where 2- and 3-bit codebooks are looked up (4-bit ones
    always use the register tables).  By default the LUT path uses LDS pair tables (two
-   weights per lookup, the table the pages' kernel keeps in shared memory) and the MFMA
-   path per-row register tables (byte permutes), the faster placement of each as measured.
-   Results agree within fp32 summation order; kept to compare the two placements. */
+   weights per lookup, the table the pages' kernel keeps in shared memory) for 2-bit
+   codebooks and for 3-bit ones in the row layout, and per-row register tables (byte
+   permutes) for 3-bit codebooks in the blocked layout; the MFMA path uses the register
+   tables: the faster placement of each as measured.  Results agree within fp32
+   summation order; kept to compare the two placements. */
 #define CBQ_PATH_REG_TABLES 0x10
 #define CBQ_PATH_LDS_TABLES 0x20
 
@@ -83,7 +85,7 @@ enum {
 /* Index layouts of cbq_weights.idx */
 enum {
   CBQ_LAYOUT_ROWS = 0,     /* one LSB-first bitstream per row (the format the method defines) */
-  CBQ_LAYOUT_BLOCKED = 1   /* the same index bits regrouped by cbq_prepack_weights */
+  CBQ_LAYOUT_BLOCKED = 1   /* the same indices regrouped (3-bit units re-encoded) by cbq_prepack_weights */
 };
 
 /*
@@ -108,8 +110,7 @@ typedef struct {
 /*
  * cbq_prepack_weights - regroup a weight set's indices for the GEMM kernels (an offline
  * step, like the codebook construction).  The values are unchanged: W[e][n][k] is the
- * same matrix, so the GEMM's results are those of the row layout (up to fp32 summation
- * order, which does not change either).
+ * same matrix, so the GEMM's results are those of the row layout, bit for bit.
  *
  * CBQ_LAYOUT_BLOCKED: with Kp = K rounded up to a multiple of 128, rows are taken in
  * groups of 16 and channels in chunks of 128; the 32 indices of row 16G + r, channels
@@ -118,7 +119,12 @@ typedef struct {
  *     ((e * N/16 + G) * Kp/128 + c) * 256*bits + (16j + r) * 4*bits.
  * So one 16-row x 128-channel tile is 256*bits contiguous bytes, which a 64-lane wave
  * reads in one fully coalesced load (a row stream would give it sixteen 16*bits-byte
- * pieces 1/8 K*bits bytes apart).
+ * pieces 1/8 K*bits bytes apart).  2- and 4-bit units keep their bytes.  A 3-bit unit
+ * (indices i0 .. i31, 12 bytes) is re-encoded so the kernels form their byte selectors
+ * with one mask or one shift and a mask: dword g (g = 0, 1, 2) holds i(8g+2b) in bits
+ * 8b .. 8b+2 and i(8g+2b+1) in bits 8b+3 .. 8b+5 (b = 0..3); the six-bit pair
+ * p_b = i(24+2b) | i(25+2b) << 3 goes to bits 8b+6 .. 8b+7 of the three dwords, bits
+ * 2w .. 2w+1 of p_b in dword w.
  *
  *  src : a CBQ_LAYOUT_ROWS weight set (device pointers).
  *  dst : device buffer of cbq_prepack_bytes(src) bytes, 16-byte aligned, not
