@@ -61,34 +61,36 @@ struct TileCtx {
   int K, g, nl, tid, rows;
 };
 
-template <int BITS, int ABITS, int NW, int NMS, bool LT, bool BLK, int BM>
+// NS: 32-column weight slots per wave (2; 1 for a single matrix in 128-column tiles).
+template <int BITS, int ABITS, int NW, int NMS, bool LT, bool BLK, int BM, int NS>
 __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint16_t (*As)[BM * LDW],
                                          const float* s_scale, const uint32_t* s_rowoff,
                                          __amdgpu_buffer_rsrc_t ores) {
   const int K = c.K, g = c.g, nl = c.nl, tid = c.tid;
   constexpr int TPR = 256 / BM;            // threads per tile row (1 or 2)
   constexpr int NPA = 8 / TPR;             // activation pieces per thread and step
-  f32x16 acc[NMS][2];
+  static_assert(NS == 2 || NW == 1, "the gate/up pair takes both slots");
+  f32x16 acc[NMS][NS];
 #pragma unroll
   for (int i = 0; i < NMS; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][s][v] = 0.0f;
   const int nk = (K + BK - 1) / BK;
   // Raw loads run two steps ahead in a ring of two slots; the step loop is unrolled
   // by two so every slot index is a compile-time constant.
-  uint32_t rw[2][2][BITS];     // [slot][matrix] raw indices
+  uint32_t rw[2][NS][BITS];    // [ring slot][weight slot] raw indices
   uint32_t ra[2][ABITS * 2 / TPR];   // [slot] raw activation codes (this thread's part of its row)
-  uint32_t bdA[2][16], bdB[2][16];  // dequantised weights, alternating between steps
+  uint32_t bdA[NS][16], bdB[NS][16];  // dequantised weights, alternating between steps
   f16x8 af[NMS];               // A fragments of the current 16-channel sub-step
 
-  auto gload = [&](int kt, uint32_t (&w)[2][BITS], uint32_t* a) {
+  auto gload = [&](int kt, uint32_t (&w)[NS][BITS], uint32_t* a) {
     const bool live = kt < nk;
     const int kb = kt * BK + g * 32;
     const bool kok = live && kb < K;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < NS; ++s)
       buf_load<4 * BITS>(c.wres[s], (c.nvalid[s] && kok) ? c.wrow_off[s] + (uint32_t)kt * c.wstep : kOffNone, w[s]);
 #pragma unroll
     for (int hh = 0; hh < 2 / TPR; ++hh) {    // this thread's 32-code halves of the step
@@ -150,19 +152,21 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   // the barrier from fragments already in registers, beside the second matrix's
   // dequantisation, so the next step's first fragment reads (which need the barrier)
   // overlap MFMAs instead of stalling.
-  auto step = [&](int kt, int buf, uint32_t (&bd)[2][16], uint32_t (&bn)[2][16],
-                  uint32_t (&wn)[2][BITS], uint32_t* an, uint32_t (&wf)[2][BITS], uint32_t* af_raw) {
+  auto step = [&](int kt, int buf, uint32_t (&bd)[NS][16], uint32_t (&bn)[NS][16],
+                  uint32_t (&wn)[NS][BITS], uint32_t* an, uint32_t (&wf)[NS][BITS], uint32_t* af_raw) {
     gload(kt + 2, wf, af_raw);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int PRE = 3 * NMS;     // MFMA pairs before the barrier
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
       const f16x8 b0 = as_f16x8(bd[0][4 * kk], bd[0][4 * kk + 1], bd[0][4 * kk + 2], bd[0][4 * kk + 3]);
-      const f16x8 b1 = as_f16x8(bd[1][4 * kk], bd[1][4 * kk + 1], bd[1][4 * kk + 2], bd[1][4 * kk + 3]);
+      const f16x8 b1 = as_f16x8(bd[NS - 1][4 * kk], bd[NS - 1][4 * kk + 1], bd[NS - 1][4 * kk + 2],
+                                bd[NS - 1][4 * kk + 3]);
 #pragma unroll
       for (int ms = 0; ms < NMS; ++ms) {
         acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
-        acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
+        if constexpr (NS == 2)
+          acc[ms][NS - 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][NS - 1], 0, 0, 0);
         af[ms] = frag(buf, kk + 1, ms);
         const int i = kk * NMS + ms;
         constexpr int NP = NPA + 4;
@@ -177,15 +181,18 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
     lds_barrier();
     {
       const f16x8 b0 = as_f16x8(bd[0][12], bd[0][13], bd[0][14], bd[0][15]);
-      const f16x8 b1 = as_f16x8(bd[1][12], bd[1][13], bd[1][14], bd[1][15]);
+      const f16x8 b1 = as_f16x8(bd[NS - 1][12], bd[NS - 1][13], bd[NS - 1][14], bd[NS - 1][15]);
 #pragma unroll
       for (int ms = 0; ms < NMS; ++ms) {
         acc[ms][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b0, acc[ms][0], 0, 0, 0);
-        acc[ms][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][1], 0, 0, 0);
+        if constexpr (NS == 2)
+          acc[ms][NS - 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], b1, acc[ms][NS - 1], 0, 0, 0);
         af[ms] = frag(buf ^ 1, 0, ms);
+        if constexpr (NS == 2) {
 #pragma unroll
-        for (int p = (4 * ms + NMS - 1) / NMS; p < (4 * (ms + 1) + NMS - 1) / NMS; ++p)
-          dq_piece(1, wn[1], bn[1], p);
+          for (int p = (4 * ms + NMS - 1) / NMS; p < (4 * (ms + 1) + NMS - 1) / NMS; ++p)
+            dq_piece(NS - 1, wn[NS - 1], bn[NS - 1], p);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -195,7 +202,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   gload(1, rw[1], ra[1]);
   astore(0, ra[0]);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     if constexpr (LT) pair_lookup32<BITS, 32, BLK>(c.ptab, c.trow[s], rw[0][s], bdA[s]);
     else dequant32<BITS, BLK>(c.tab[s], rw[0][s], bdA[s]);
   }
@@ -213,9 +220,9 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
   // Stores go through a buffer resource: rows past the tile (kOffNone) and columns
   // past N (kOffCol) carry out-of-range offsets and are dropped without branches.
   constexpr uint32_t ESZ = NW == 2 ? 2 : 4;
-  uint32_t coff[2];
+  uint32_t coff[NS];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) coff[s] = c.nvalid[s] ? (uint32_t)c.nrow[s] * ESZ : kOffCol;
+  for (int s = 0; s < NS; ++s) coff[s] = c.nvalid[s] ? (uint32_t)c.nrow[s] * ESZ : kOffCol;
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
@@ -231,7 +238,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int v = 4 * q + j;
-          const float gv = acc[ms][0][v] * sc[j], uv = acc[ms][1][v] * sc[j];
+          const float gv = acc[ms][0][v] * sc[j], uv = acc[ms][NS - 1][v] * sc[j];
           hb[j] = f32_to_bf16_rne(silu_mul(gv, uv));
         }
         const bool odd = (nl & 1) != 0;
@@ -248,7 +255,7 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
         for (int j = 0; j < 4; ++j) {
           const int v = 4 * q + j;
 #pragma unroll
-          for (int s = 0; s < 2; ++s) buf_store_f32(ores, ro[j] + coff[s], acc[ms][s][v] * sc[j]);
+          for (int s = 0; s < NS; ++s) buf_store_f32(ores, ro[j] + coff[s], acc[ms][s][v] * sc[j]);
         }
       }
     }
@@ -256,8 +263,10 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
 }
 
 // BLK: 3-bit indices in the blocked layout's re-encoded units (cbq_prepack_weights).
-template <int BITS, int ABITS, int NW, bool LT, bool BLK, int BM = tile_rows<BITS>()>
-__global__ void __launch_bounds__(256, 256 / BM)
+// NS: 32-column weight slots per wave (1: a single matrix in 128-column tiles, twice the
+// workgroups and half the accumulators, so two workgroups share each CU at BM = 256 too).
+template <int BITS, int ABITS, int NW, bool LT, bool BLK, int NS, int BM = tile_rows<BITS>()>
+__global__ void __launch_bounds__(256, (BM == 128 || NS == 1) ? 2 : 1)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
@@ -377,10 +386,11 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const int lane = tid & 63, wave = tid >> 6;
   c.nl = lane & 31;
   c.g = lane >> 5;
-  constexpr int NCOL = (NW == 2) ? 128 : 256;        // weight rows per matrix per tile
+  constexpr int NCOL = (NW == 2) ? 128 : 128 * NS;   // weight rows per matrix per tile
   const int n0 = tcol * NCOL;
   if constexpr (NW == 2) { c.nrow[0] = c.nrow[1] = n0 + wave * 32 + c.nl; }   // gate, up
-  else { c.nrow[0] = n0 + wave * 64 + c.nl; c.nrow[1] = c.nrow[0] + 32; }
+  else if constexpr (NS == 2) { c.nrow[0] = n0 + wave * 64 + c.nl; c.nrow[1] = c.nrow[0] + 32; }
+  else { c.nrow[0] = c.nrow[1] = n0 + wave * 32 + c.nl; }
   constexpr int L = 1 << BITS;
   // bytes per row of the expert's index block (rows layout: each row's bitstream; blocked
   // layout: 16-row x 128-channel tiles of 256*BITS bytes, a step of 64 channels being half
@@ -389,7 +399,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   c.wstep = blocked ? 128u * BITS : 8u * BITS;
   c.ptab = Tab;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const GemmW& W = (NW == 2 && s == 1) ? w1 : w0;
     c.nvalid[s] = c.nrow[s] < N;
     const int64_t rowi = (int64_t)e * N + (c.nvalid[s] ? c.nrow[s] : 0);
@@ -414,17 +424,17 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // output buffer: every row of this call (n_rows) x ldo elements
   const __amdgpu_buffer_rsrc_t ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
   switch (nms) {
-    case 1: tile_run<BITS, ABITS, NW, 1, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
-    case 2: tile_run<BITS, ABITS, NW, 2, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
-    case 3: tile_run<BITS, ABITS, NW, 3, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
-    case 4: tile_run<BITS, ABITS, NW, 4, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+    case 1: tile_run<BITS, ABITS, NW, 1, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
+    case 2: tile_run<BITS, ABITS, NW, 2, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
+    case 3: tile_run<BITS, ABITS, NW, 3, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
+    case 4: tile_run<BITS, ABITS, NW, 4, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
     default:
       if constexpr (BM == 256) {
         switch (nms) {
-          case 5: tile_run<BITS, ABITS, NW, 5, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
-          case 6: tile_run<BITS, ABITS, NW, 6, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
-          case 7: tile_run<BITS, ABITS, NW, 7, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
-          default: tile_run<BITS, ABITS, NW, 8, LT, BLK, BM>(c, As, s_scale, s_rowoff, ores); break;
+          case 5: tile_run<BITS, ABITS, NW, 5, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
+          case 6: tile_run<BITS, ABITS, NW, 6, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
+          case 7: tile_run<BITS, ABITS, NW, 7, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
+          default: tile_run<BITS, ABITS, NW, 8, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
         }
       }
       break;
@@ -435,21 +445,31 @@ template <int BITS, int ABITS, bool LT, bool BLK>
 static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream) {
   constexpr int BM = tile_rows<BITS>();
   const int E = a.offsets ? a.E : 1;
-  const int ncol = a.n_w == 2 ? 128 : 256;
   // M-tile slots: an expert of r rows takes ceil(r / BM) <= r / BM + 1 of them, and only
   // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them
   const int64_t big = a.offsets ? std::min<int64_t>(E, a.n_rows / (min_rows + 1)) : 0;
-  int64_t mtiles = (a.n_rows + BM - 1) / BM + big;
-  mtiles = (mtiles + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG M-tiles on each XCD
-  dim3 grid((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles);
-  if (a.n_w == 2)
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK>), grid, dim3(256), 0, stream, a.codes,
-                       a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
+  const int64_t mt = (a.n_rows + BM - 1) / BM + big;
+  const int64_t mtiles = (mt + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG M-tiles per XCD
+  auto grid_for = [&](int ncol) { return dim3((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles); };
+  if (a.n_w == 2) {
+    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK, 2>), grid_for(128), dim3(256), 0, stream,
+                       a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
                        min_rows, a.blocked, a.out, a.ldo);
-  else
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK>), grid, dim3(256), 0, stream, a.codes,
-                       a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                       min_rows, a.blocked, a.out, a.ldo);
+    return hipGetLastError();
+  }
+  if constexpr (BM == 256) {
+    // a single matrix whose 256-column tiles would leave CUs idle (fewer than two
+    // workgroups per CU even with every M-tile slot filled) takes 128-column tiles
+    if ((int64_t)((a.N + 255) / 256) * mt < 2 * 256) {
+      hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 1>), grid_for(128), dim3(256), 0, stream,
+                         a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
+                         min_rows, a.blocked, a.out, a.ldo);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 2>), grid_for(256), dim3(256), 0, stream,
+                     a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
+                     min_rows, a.blocked, a.out, a.ldo);
   return hipGetLastError();
 }
 
