@@ -21,6 +21,8 @@
 //  - A larger expert is split along rows: wave w takes row blocks w, w + splitk, ...
 //    over all of K; the waves of a workgroup read the same index bytes at about the
 //    same time, so the repeats are served by the caches.
+#include <type_traits>
+
 #include "cbq_internal.hpp"
 
 namespace cbq {
@@ -159,95 +161,75 @@ lut_decode_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ s
     }
     const int nsub = (int)min<int64_t>((me - mb + 15) >> 4, MSUB);
 
-    // ring of DEPTH chunks of raw data, loaded DEPTH chunks ahead: a wave of few chunks
-    // (the split-K waves of small grids) has all of its loads in flight at once
-    struct Slot {
-      uint32_t w[NG][NW][BITS];
-      uint32_t a[MSUB][ABITS];
-    };
-    Slot ring[DEPTH];
-    auto load = [&](int c, Slot& d) {
-      const bool ok = c < c_end && c * 128 + g * 32 < K;
+    // The K sweep for NSUB live token sub-tiles, a compile-time count: an expert with
+    // fewer rows than MSUB sub-tiles hold issues no loads, conversions or MFMAs for the
+    // empty ones.  A ring of DEPTH chunks of raw data is loaded DEPTH chunks ahead, so a
+    // wave of few chunks (the split-K waves of small grids) has all its loads in flight.
+    auto sweep = [&](auto nsub_c) {
+      constexpr int NSUB = decltype(nsub_c)::value;
+      struct Slot {
+        uint32_t w[NG][NW][BITS];
+        uint32_t a[NSUB][ABITS];
+      };
+      Slot ring[DEPTH];
+      auto load = [&](int c, Slot& d) {
+        const bool ok = c < c_end && c * 128 + g * 32 < K;
 #pragma unroll
-      for (int q = 0; q < NG; ++q)
+        for (int q = 0; q < NG; ++q)
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-          buf_load<4 * BITS>(wres[w], ok ? wlane[q] : kOffNone, d.w[q][w], (uint32_t)c * chunk_step);
-      const uint32_t cs = (uint32_t)(c * 128 * ABITS / 8);
+          for (int w = 0; w < NW; ++w)
+            buf_load<4 * BITS>(wres[w], ok ? wlane[q] : kOffNone, d.w[q][w], (uint32_t)c * chunk_step);
+        const uint32_t cs = (uint32_t)(c * 128 * ABITS / 8);
 #pragma unroll
-      for (int s = 0; s < MSUB; ++s) {
+        for (int s = 0; s < NSUB; ++s) {
 #pragma unroll
-        for (int h = 0; h < ABITS / 4; ++h)
-          buf_load<16>(cres, ok ? aoff[s] + 16 * h : kOffNone, &d.a[s][4 * h], cs);
-      }
-    };
-    // the activation fragments are converted once per chunk and shared by the row groups
-    auto chunk = [&](const Slot& cur) {
-      if constexpr (NG == 1) {
-        // one row group: convert each token sub-tile just before its MFMAs
-        uint32_t bd[NW][16];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          if constexpr (LT) pair_lookup32<BITS, 16, BLK>(ptab, trow[0][w], cur.w[0][w], bd[w]);
-          else dequant32<BITS, BLK>(tab[0][w], cur.w[0][w], bd[w]);
+          for (int h = 0; h < ABITS / 4; ++h)
+            buf_load<16>(cres, ok ? aoff[s] + 16 * h : kOffNone, &d.a[s][4 * h], cs);
         }
+      };
+      // the activation fragments are converted once per chunk and shared by the row
+      // groups and weight matrices
+      auto chunk = [&](const Slot& cur) {
+        uint32_t ad[NSUB][16];
 #pragma unroll
-        for (int s = 0; s < MSUB; ++s) {
-          if (s >= nsub) break;
-          uint32_t ad[16];
-          codes32_to_f16_ord<ABITS, LT>(cur.a[s], ad);
+        for (int s = 0; s < NSUB; ++s) codes32_to_f16_ord<ABITS, LT>(cur.a[s], ad[s]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f16x8 A = as_f16x8(ad[4 * j], ad[4 * j + 1], ad[4 * j + 2], ad[4 * j + 3]);
+        for (int q = 0; q < NG; ++q) {
+          uint32_t bd[NW][16];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-              const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
-              acc[0][w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[0][w][s], 0, 0, 0);
-            }
+          for (int w = 0; w < NW; ++w) {
+            if constexpr (LT) pair_lookup32<BITS, 16, BLK>(ptab, trow[q][w], cur.w[q][w], bd[w]);
+            else dequant32<BITS, BLK>(tab[q][w], cur.w[q][w], bd[w]);
           }
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int w = 0; w < NW; ++w) {
+                const f16x8 A = as_f16x8(ad[s][4 * j], ad[s][4 * j + 1], ad[s][4 * j + 2], ad[s][4 * j + 3]);
+                const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
+                acc[q][w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[q][w][s], 0, 0, 0);
+              }
         }
-        return;
-      }
-      uint32_t ad[MSUB][16];
+      };
 #pragma unroll
-      for (int s = 0; s < MSUB; ++s)
-        if (s < nsub) codes32_to_f16_ord<ABITS, LT>(cur.a[s], ad[s]);
+      for (int i = 0; i < DEPTH; ++i) load(c_begin + i, ring[i]);
+      int c = c_begin;
+      for (; c + DEPTH - 1 < c_end; c += DEPTH) {
 #pragma unroll
-      for (int q = 0; q < NG; ++q) {
-        uint32_t bd[NW][16];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          if constexpr (LT) pair_lookup32<BITS, 16, BLK>(ptab, trow[q][w], cur.w[q][w], bd[w]);
-          else dequant32<BITS, BLK>(tab[q][w], cur.w[q][w], bd[w]);
-        }
-#pragma unroll
-        for (int s = 0; s < MSUB; ++s) {
-          if (s >= nsub) break;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f16x8 A = as_f16x8(ad[s][4 * j], ad[s][4 * j + 1], ad[s][4 * j + 2], ad[s][4 * j + 3]);
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-              const f16x8 B = as_f16x8(bd[w][4 * j], bd[w][4 * j + 1], bd[w][4 * j + 2], bd[w][4 * j + 3]);
-              acc[q][w][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[q][w][s], 0, 0, 0);
-            }
-          }
+        for (int i = 0; i < DEPTH; ++i) {
+          chunk(ring[i]);
+          load(c + DEPTH + i, ring[i]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < DEPTH - 1; ++i)
+        if (c + i < c_end) chunk(ring[i]);
     };
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) load(c_begin + i, ring[i]);
-    int c = c_begin;
-    for (; c + DEPTH - 1 < c_end; c += DEPTH) {
-#pragma unroll
-      for (int i = 0; i < DEPTH; ++i) {
-        chunk(ring[i]);
-        load(c + DEPTH + i, ring[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < DEPTH - 1; ++i)
-      if (c + i < c_end) chunk(ring[i]);
+    static_assert(MSUB == 1 || MSUB == 2, "one or two token sub-tiles");
+    if (MSUB == 2 && nsub == 2) sweep(std::integral_constant<int, MSUB>{});
+    else sweep(std::integral_constant<int, 1>{});
 
     // ordered split-K reduction
     if (ksplit) {
