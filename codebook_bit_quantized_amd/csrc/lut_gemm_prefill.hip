@@ -22,8 +22,9 @@
 // fewer than 32 rows.  A is double-buffered in LDS (converted by one or two threads per
 // row) and the next step's loads are issued before this step's MFMAs.
 //
-// A tile is one column range x the y-th BM-row slice in expert order, skipping
-// experts with at most min_rows rows (those go to the decode path).
+// A tile is one column range x one BM-row slice of an expert, skipping experts with at
+// most min_rows rows (those go to the decode path); an expert's slices go to the XCDs in
+// runs that share its weights in one L2.
 #include <algorithm>
 
 #include "cbq_internal.hpp"
@@ -281,16 +282,17 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   __shared__ int s_e;
 
   const int tid = threadIdx.x;
-  // ---- workgroup -> tile (M-tile ty, column tile tcol) ----
+  // ---- workgroup -> (M-tile, column tile tcol) ----
   // The hardware deals workgroups to the 8 XCDs round-robin by linear id, so XCD x
   // gets ids x, x + 8, ...; those ids work through rounds of gridDim.x column tiles
   // of one M-tile each, so the column tiles of an M-tile (same activation rows) share
-  // one L2.  Rounds G*P .. G*P + G - 1 of XCD x take the M-tiles G*(8P + x) .. + G - 1:
-  // runs of G consecutive M-tiles (mostly of one expert: the same weights) stay on one
-  // XCD.  G is the largest power of two <= XG with 8G <= T, the call's M-tile count
-  // (counted first), so a call of few tiles still spreads them over all eight XCDs.
-  // (The host makes the M-tile slots a multiple of 8 * XG, XG a power of two, so the
-  // slots map one to one onto M-tiles 0 .. slots - 1.)
+  // one L2.  Each expert's M-tiles are cut into runs of G consecutive tiles (its last
+  // run may be shorter; no run spans two experts), and rounds G*P .. G*P + G - 1 of
+  // XCD x take the tiles of run 8P + x: one L2 fetches an expert's weights once per run.
+  // G is the largest power of two <= XG with 8G <= T, the call's M-tile count (counted
+  // first), so a call of few tiles still spreads them over all eight XCDs.  Rounds past
+  // the end of a short run have no work.  (The host makes the slots a multiple of
+  // 8 * XG, XG a power of two, and leaves room for a partial run per expert.)
   if (tid < 64) {
     int64_t tot = 0;
     if (!offsets) {
@@ -315,35 +317,38 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
   const uint32_t q = (lin / 8) / gridDim.x;
   const uint32_t P = q / G;
-  const int64_t ty = (int64_t)G * (8 * (int64_t)P + lin % 8) + (q % G);
+  const int64_t run = 8 * (int64_t)P + lin % 8, rr = q % G;   // run, tile of the run
   const int tcol = (int)((lin / 8) % gridDim.x);
-  // ---- M-tile -> (expert, first row): wave 0 scans the experts' tile counts ----
+  // ---- (run, tile of the run) -> (expert, first row): wave 0 scans the experts' run counts ----
   if (tid < 64) {
     if (!offsets) {
-      if (tid == 0) {
+      if (tid == 0) {                                // one matrix of n_rows rows: runs are contiguous
+        const int64_t ty = run * G + rr;
         const bool ok = ty * BM < n_rows;
         s_e = ok ? 0 : -1; s_r0 = 0; s_me = n_rows; s_m0 = ty * BM;
       }
     } else {
       if (tid == 0) s_e = -1;
-      int64_t before = 0;                            // tiles of earlier 64-expert chunks
+      int64_t before = 0;                            // runs of earlier 64-expert chunks
       for (int base = 0; base < E; base += 64) {
         const int ex = base + tid;
         int64_t a = 0, cnt = 0;
         if (ex < E) { a = offsets[ex]; cnt = offsets[ex + 1] - a; }
         const int64_t nt = cnt > min_rows ? (cnt + BM - 1) / BM : 0;
-        int64_t incl = nt;                           // inclusive scan over the wave
+        const int64_t nr = (nt + G - 1) / G;         // the expert's runs
+        int64_t incl = nr;                           // inclusive scan over the wave
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           const int64_t o = __shfl_up(incl, d);
           if (tid >= d) incl += o;
         }
-        const int64_t lo = before + incl - nt;
-        if (nt > 0 && ty >= lo && ty < lo + nt) {
-          s_e = ex; s_r0 = a; s_me = cnt; s_m0 = (ty - lo) * BM;
+        const int64_t lo = before + incl - nr;
+        if (nr > 0 && run >= lo && run < lo + nr) {
+          const int64_t tile = (run - lo) * G + rr;  // past the expert's last tile: no work
+          if (tile < nt) { s_e = ex; s_r0 = a; s_me = cnt; s_m0 = tile * BM; }
         }
         before += __shfl(incl, 63);
-        if (before > ty) break;
+        if (before > run) break;
       }
     }
   }
@@ -445,11 +450,13 @@ template <int BITS, int ABITS, bool LT, bool BLK>
 static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream) {
   constexpr int BM = tile_rows<BITS>();
   const int E = a.offsets ? a.E : 1;
-  // M-tile slots: an expert of r rows takes ceil(r / BM) <= r / BM + 1 of them, and only
-  // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them
+  // M-tile slots: an expert of r rows takes ceil(r / BM) <= r / BM + 1 tiles, and only
+  // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them;
+  // its runs of G <= XG tiles take at most XG - 1 slots more
   const int64_t big = a.offsets ? std::min<int64_t>(E, a.n_rows / (min_rows + 1)) : 0;
   const int64_t mt = (a.n_rows + BM - 1) / BM + big;
-  const int64_t mtiles = (mt + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG M-tiles per XCD
+  const int64_t slots = mt + big * (XG - 1);
+  const int64_t mtiles = (slots + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG slots per XCD
   auto grid_for = [&](int ncol) { return dim3((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles); };
   if (a.n_w == 2) {
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK, 2>), grid_for(128), dim3(256), 0, stream,
