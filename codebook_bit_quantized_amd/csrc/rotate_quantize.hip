@@ -7,8 +7,9 @@
 // token takes G lanes, G the power of two >= K/32 when K <= 1024 (then 64/G tokens
 // share a wave), else a whole workgroup of ceil(K/2048) waves.  Between 1024 and
 // 2048 channels with K/32 not a power of two, tokens of K/32 lanes are packed back to
-// back in 1024-lane workgroups (a token may straddle two waves; its absmax then
-// meets in LDS), which keeps all but K/32 - 1 lanes of a workgroup busy.  The transform runs
+// back in 512-lane workgroups (a token may straddle two waves; its absmax then meets in
+// LDS), which keeps all but K/32 - 1 lanes of a workgroup busy; workgroups of eight
+// waves, four to a CU, drift out of step, so one's loads overlap another's arithmetic.  The transform runs
 // in fp64, which is exact for bf16 inputs whose nonzero exponents in a block spread
 // at most 45 - log2(b) binades: five butterfly stages inside the thread, then one
 // lane exchange per further stage (DPP for lane distances 1, 2 and 8, ds_swizzle for
@@ -331,7 +332,7 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
   size_t lds = 0;
   if (nthr > 32 && nthr < 64) {
     G = 0;                                   // packed: K/32 lanes per token
-    threads = 1024;
+    threads = 512;
     const int64_t per_block = threads / nthr;
     blocks = (T + per_block - 1) / per_block;
   } else if (nthr <= 64) {
