@@ -37,7 +37,7 @@ namespace {
 // 128 (two threads per row, two workgroups a CU) for 2- and 3-bit codebooks.
 template <int BITS>
 constexpr int tile_rows() { return BITS == 4 ? 256 : 128; }
-constexpr int XG = 4;       // consecutive M-tiles kept on one XCD
+constexpr int XG = 4;       // consecutive M-tiles kept on one XCD (the padding counts below take XG <= 4)
 constexpr int BK = 64;      // channels per step
 constexpr int LDW = BK + 8; // fp16 per LDS row (padding staggers the banks)
 
@@ -279,6 +279,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   __shared__ __attribute__((aligned(16))) float s_scale[BM];
   __shared__ __attribute__((aligned(16))) uint32_t s_rowoff[BM];   // byte offset of each row in out
   __shared__ int64_t s_r0, s_me, s_m0, s_ttot;
+  __shared__ uint32_t s_pad;
   __shared__ int s_e;
 
   const int tid = threadIdx.x;
@@ -290,30 +291,45 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // run may be shorter; no run spans two experts), and rounds G*P .. G*P + G - 1 of
   // XCD x take the tiles of run 8P + x: one L2 fetches an expert's weights once per run.
   // G is the largest power of two <= XG with 8G <= T, the call's M-tile count (counted
-  // first), so a call of few tiles still spreads them over all eight XCDs.  Rounds past
-  // the end of a short run have no work.  (The host makes the slots a multiple of
-  // 8 * XG, XG a power of two, and leaves room for a partial run per expert.)
+  // first), so a call of few tiles still spreads them over all eight XCDs, and with at
+  // most T / 4 slots of padding.  Rounds past the end of a short run, or past the call's
+  // last run, have no work.  (The host makes the slots a multiple of 8 G' for a power of
+  // two G' >= G and leaves room for a partial run per expert.)
   if (tid < 64) {
+    // the call's M-tiles, and the slots that runs of 2 and of 4 tiles would leave empty
+    // at the end of each expert (16-bit fields; they only steer the run length below)
     int64_t tot = 0;
+    uint32_t pad = 0;
     if (!offsets) {
       tot = n_rows > min_rows ? (n_rows + BM - 1) / BM : 0;
+      pad = (uint32_t)((-tot) & 1) | ((uint32_t)((-tot) & 3) << 16);
     } else {
       for (int base = 0; base < E; base += 64) {
         const int ex = base + tid;
         int64_t cnt = 0;
         if (ex < E) cnt = offsets[ex + 1] - offsets[ex];
         int64_t nt = cnt > min_rows ? (cnt + BM - 1) / BM : 0;
+        uint32_t pd = (uint32_t)((-nt) & 1) | ((uint32_t)((-nt) & 3) << 16);
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) nt += __shfl_xor(nt, d);
+        for (int d = 1; d < 64; d <<= 1) {
+          nt += __shfl_xor(nt, d);
+          pd += __shfl_xor(pd, d);
+        }
         tot += nt;
+        pad += pd;
       }
     }
-    if (tid == 0) s_ttot = tot;
+    if (tid == 0) { s_ttot = tot; s_pad = pad; }
   }
   __syncthreads();
   const int64_t ttot = s_ttot;
   uint32_t G = 1;                                    // a power of two, so it divides the
-  while (2 * G <= XG && 8 * 2 * G <= ttot) G *= 2;   // rounds per XCD (a multiple of XG)
+  while (2 * G <= XG && 8 * 2 * G <= ttot) G *= 2;   // rounds per XCD
+  // shorter runs where padding each expert's last run would leave more than a quarter
+  // of the slots empty (experts of one or two tiles): empty slots between the busy ones
+  // would crowd the busy workgroups onto fewer CUs.  (Any power of two up to the
+  // host's bound is a valid choice; this one only steers the placement.)
+  while (G > 1 && (int64_t)(G == 4 ? s_pad >> 16 : s_pad & 0xFFFFu) > ttot / 4) G >>= 1;
   const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
   const uint32_t q = (lin / 8) / gridDim.x;
   const uint32_t P = q / G;
@@ -451,12 +467,17 @@ static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream)
   constexpr int BM = tile_rows<BITS>();
   const int E = a.offsets ? a.E : 1;
   // M-tile slots: an expert of r rows takes ceil(r / BM) <= r / BM + 1 tiles, and only
-  // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them;
-  // its runs of G <= XG tiles take at most XG - 1 slots more
+  // experts of more than min_rows rows get any, at most n_rows / (min_rows + 1) of them.
+  // The kernel's run length G follows from the call's tile count by the rule below; taken
+  // at this upper bound it bounds the kernel's G (powers of two, so whole runs of this
+  // length are whole runs of the kernel's), and each expert's last run leaves at most
+  // G - 1 slots unused
   const int64_t big = a.offsets ? std::min<int64_t>(E, a.n_rows / (min_rows + 1)) : 0;
   const int64_t mt = (a.n_rows + BM - 1) / BM + big;
-  const int64_t slots = mt + big * (XG - 1);
-  const int64_t mtiles = (slots + 8 * XG - 1) / (8 * XG) * (8 * XG);   // whole runs of XG slots per XCD
+  int64_t G = 1;
+  while (2 * G <= XG && 8 * 2 * G <= mt) G *= 2;
+  const int64_t slots = mt + big * (G - 1);
+  const int64_t mtiles = (slots + 8 * G - 1) / (8 * G) * (8 * G);   // whole runs on every XCD
   auto grid_for = [&](int ncol) { return dim3((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles); };
   if (a.n_w == 2) {
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK, 2>), grid_for(128), dim3(256), 0, stream,
