@@ -262,6 +262,65 @@ def test_many_tile_decode_gemm(bits, act_bits, n_w, path):
         assert_normwise(out.cpu().numpy(), ref[0], 1e-3, "f32")
 
 
+def _prefill_run_length(counts, bm, min_rows):
+    """The run length the MFMA kernel picks for these expert row counts: the largest power of
+    two <= 4 with 8G <= the call's tile count T, then halved while padding each expert's last
+    run to G tiles would leave more than T / 4 slots empty."""
+    nt = np.where(counts > min_rows, (counts + bm - 1) // bm, 0)
+    t = int(nt.sum())
+    g = 1
+    while 2 * g <= 4 and 16 * g <= t:
+        g *= 2
+    while g > 1 and int(((-nt) % g).sum()) > t // 4:
+        g //= 2
+    return g
+
+
+# Expert row counts for the MFMA GEMM's placement of M-tiles on the XCDs: 80 experts (the
+# tile scan works through experts 64 at a time), experts of several runs on both sides of
+# expert 64, empty experts, and one set for each run length the kernel can pick.
+_RUN_CASES = {
+    # long experts only: runs of 4 (3-bit tiles of 128 rows), of 2 (4-bit tiles of 256)
+    "long": {2: 1100, 10: 260, 30: 512, 65: 520, 70: 900, 79: 1024},
+    # plus three one-tile experts: padding halves the runs of 4
+    "mixed": {2: 1100, 10: 260, 30: 512, 65: 520, 70: 900, 79: 1024, 5: 90, 40: 70, 77: 100},
+    # mostly one-tile experts: runs of one
+    "short": {1: 1100, 66: 700, **{e: 40 + e for e in range(20, 60, 2)}},
+}
+
+
+@pytest.mark.parametrize("case", sorted(_RUN_CASES))
+@pytest.mark.parametrize("bits,act_bits,n_w", [(3, 4, 2), (4, 8, 2), (3, 4, 1), (4, 4, 1)])
+@pytest.mark.parametrize("path", [cbq.PATH_MFMA, cbq.PATH_AUTO])
+def test_prefill_run_placement(case, bits, act_bits, n_w, path):
+    E, N, K, T = 80, 272, 96, 600
+    counts = np.zeros(E, dtype=np.int64)
+    for e, c in _RUN_CASES[case].items():
+        counts[e] = c
+    if path == cbq.PATH_AUTO:
+        counts[[7, 50, 71]] = [1, 32, 17]       # experts AUTO sends to the LUT path
+    bm = 256 if bits == 4 else 128
+    min_rows = cbq.AUTO_MAX_LUT_ROWS if path == cbq.PATH_AUTO else 0
+    want_g = {("long", 128): 4, ("long", 256): 2, ("mixed", 128): 2, ("mixed", 256): 2,
+              ("short", 128): 1, ("short", 256): 1}[(case, bm)]
+    assert _prefill_run_length(counts, bm, min_rows) == want_g
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    rng = np.random.default_rng(bits * 100 + act_bits * 10 + n_w + len(case))
+    row_token = rng.integers(0, T, R).astype(np.int32)
+    rq = oracle.rotate_quantize(datagen.random_tokens(700 + bits, T, K), 0, act_bits)
+    ws = [datagen.random_weights(80 + bits + m, E, N, K, bits, keep_raw=False) for m in range(n_w)]
+    out = cbq.codebook_lut_gemm(to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits,
+                                [upload_weights(w) for w in ws], expert_offsets=to_dev(offsets),
+                                row_token=to_dev(row_token), path=path)
+    ref = [oracle.expert_gemm(rq["q"], rq["scale"], row_token, offsets, w.idx, w.codebook, K, bits)
+           for w in ws]
+    if n_w == 2:
+        assert_bf16_close(bf16_to_bits(out), oracle.silu_mul_bf16(ref[0], ref[1]), f"swiglu {case}")
+    else:
+        assert_normwise(out.cpu().numpy(), ref[0], 1e-3, f"f32 {case}")
+
+
 @pytest.mark.parametrize("bits,act_bits", [(3, 4), (4, 8)])
 def test_swiglu_paths_agree(bits, act_bits):
     """Both GEMM paths end in the same SwiGLU formula; only the fp32 summation order of g
