@@ -37,7 +37,8 @@ namespace {
 // 128 (two threads per row, two workgroups a CU) for 2- and 3-bit codebooks.
 template <int BITS>
 constexpr int tile_rows() { return BITS == 4 ? 256 : 128; }
-constexpr int XG = 4;       // consecutive M-tiles kept on one XCD (the padding counts below take XG <= 4)
+constexpr int XG = 4;       // consecutive M-tiles kept on one XCD
+static_assert(XG == 1 || XG == 2 || XG == 4, "the kernel counts the padding of runs of 2 and 4 only");
 constexpr int BK = 64;      // channels per step
 constexpr int LDW = BK + 8; // fp16 per LDS row (padding staggers the banks)
 
