@@ -582,7 +582,8 @@ def bench_kmeans(args, cbq, torch):
 
 def bench_peaks(args, torch):
     """Measured ceilings beside the vendor figures used as roofline peaks: HBM with a
-    plain 1 GiB device copy and a 1 GiB read (a sum), and the fp16/bf16 matrix cores
+    plain 1 GiB device copy and a 1 GiB read (a sum), cold launch and read floors at the
+    decode GEMMs' sizes, and the fp16/bf16 matrix cores
     with library GEMMs (torch.matmul, which calls hipBLASLt), at a large square shape
     and at the 8-expert layer's per-expert shapes (about 128 rows per expert)."""
     dev = "cuda:0"
@@ -607,6 +608,20 @@ def bench_peaks(args, torch):
     hbm = dict(copy_GBs=round(2 * n / (copy_ms / 1000) / 1e9, 1),
                read_GBs=round(n / (read_ms / 1000) / 1e9, 1))
 
+    # cold floors, each launch after the decode measurements' read flush: a trivial kernel
+    # (launch and cold fetch of the kernel itself), and plain reads (sums) of the bytes of
+    # the dense 2560 -> 9728 decode at T = 16 and of the headline decode gate/up
+    flush = CacheFlush(torch, dev, "read")
+    tiny = torch.zeros(1, device=dev)
+    cold = dict(trivial_kernel_us=round(cold_us(torch, flush, lambda: tiny.add_(1), 30), 2))
+    for name, nbytes in (("read_13MB", 13_406_272), ("read_144MB", 144_258_176)):
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        out = torch.zeros(1, dtype=torch.float32, device=dev)
+        us = cold_us(torch, flush, lambda: torch.sum(buf, dim=0, out=out[0]), 30)
+        cold[name] = dict(bytes=nbytes, us=round(us, 2), GBs=round(nbytes / us / 1e3, 1))
+        del buf
+    del flush
+
     gemms = {}
     shapes = [("square_8192", 8192, 8192, 8192),
               ("moe8_gate_up_M128", 128, 4096, 2 * 14336),
@@ -621,7 +636,7 @@ def bench_peaks(args, torch):
             gemms[f"{dt_name}_{name}"] = dict(M=M, K=K, N=N, us=round(ms * 1000, 1),
                                                TFLOPs=round(2 * M * K * N / (ms / 1000) / 1e12, 1))
             del a, b
-    line = dict(mode="peaks", hbm=hbm, hbm_vendor_GBs=HBM_PEAK_GBS,
+    line = dict(mode="peaks", hbm=hbm, cold=cold, hbm_vendor_GBs=HBM_PEAK_GBS,
                 hbm_copy_frac_of_vendor=round(hbm["copy_GBs"] / HBM_PEAK_GBS, 3),
                 hbm_read_frac_of_vendor=round(hbm["read_GBs"] / HBM_PEAK_GBS, 3),
                 gemm=gemms, mfma_vendor_TFLOPs=F16_MFMA_PEAK_TFLOPS,
