@@ -57,8 +57,9 @@ def test_rotate_quantize_explicit_blocks_and_stride(had_block):
 @pytest.mark.parametrize("K,had_block,act_bits", [(1056, 0, 4), (1088, 0, 8), (1408, 0, 4), (1536, 0, 8),
                                                    (1984, 0, 4), (1408, 8, 8), (1408, 32, 4)])
 def test_rotate_quantize_packed_tokens(K, had_block, act_bits):
-    # K/32 lanes per token, not a power of two: tokens packed back to back, some of
-    # them straddling two waves; 50 tokens fill two workgroups and part of a third
+    # K/32 lanes per token, not a power of two: tokens packed back to back in 512-lane
+    # workgroups (8 to 15 tokens each), some of them straddling two waves; 50 tokens fill
+    # several workgroups and part of another
     T = 50
     xb = datagen.random_tokens(K + 3 * act_bits, T, K + 32)  # ldx = K + 32
     xb[7] = 0                                                # an all-zero token
@@ -238,13 +239,14 @@ def test_many_tile_decode_gemm(bits, act_bits, n_w, path):
     # 64 experts x 2080 rows: enough 16-row tiles that no wave splits K (the decode
     # layout of the large MoE layers); K = 160 leaves a 32-channel chunk tail, N = 2080
     # leaves part of the last two-group wave empty, and the row counts include
-    # empty experts, full 32-row blocks and one expert of 40 rows (two row blocks when
-    # forced onto the LUT path; AUTO sends it to the MFMA path)
+    # empty experts, full 32-row blocks, 16 and 17 rows (one sub-tile, and a second one of
+    # one row), and experts of 33 and 40 rows (a second row block, of one and of eight
+    # rows, when forced onto the LUT path; AUTO sends them to the MFMA path)
     E, N, K, T = 64, 2080, 160, 50
     rng = np.random.default_rng(bits * 10 + act_bits + n_w)
     counts = rng.integers(0, 6, E)
     counts[[3, 17, 40]] = 0
-    counts[5], counts[9], counts[63] = 32, 16, 40
+    counts[5], counts[9], counts[12], counts[20], counts[63] = 32, 16, 17, 33, 40
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(offsets[-1])
     row_token = rng.integers(0, T, R).astype(np.int32)
