@@ -151,10 +151,13 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
         for (int i = 0; i < 4; ++i) f[4 * h + i] = __fmul_rn(f[4 * h + i], m[i]);
       }
     }
-    uint32_t sg = 0;
-    if (signs != nullptr && active) sg = reinterpret_cast<const uint32_t*>(signs)[j];
+    if (signs != nullptr && active) {
+      const uint32_t sg = reinterpret_cast<const uint32_t*>(signs)[j];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = (double)((sg >> i) & 1u ? -f[i] : f[i]);
+      for (int i = 0; i < 32; ++i) f[i] = (sg >> i) & 1u ? -f[i] : f[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = (double)f[i];
   }
 
   // ---- optional exactness check: exponent spread inside each block ----
@@ -291,26 +294,27 @@ rotate_quantize_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, i
     const float r = (float)((double)u[i] * rs);
     q[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(r + kMagic, kMagic + lo, kMagic + Q));
   }
+  // the low byte of each q[i] is the code as an int8; byte permutes gather them
+  auto low_bytes = [&](int i0, int i1, int i2, int i3) {   // bytes (q[i0], q[i1], q[i2], q[i3])
+    const uint32_t lo = __builtin_amdgcn_perm(q[i1], q[i0], 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(q[i3], q[i2], 0x0C0C0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  };
   if (active) {
     if (act_bits == 4) {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t d = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d |= (q[8 * k + i] & 0xFu) << (4 * i);
-        w[k] = d;
+        // byte b holds code 2b in its low nibble and code 2b + 1 in its high one
+        const uint32_t ev = low_bytes(8 * k, 8 * k + 2, 8 * k + 4, 8 * k + 6);
+        const uint32_t od = low_bytes(8 * k + 1, 8 * k + 3, 8 * k + 5, 8 * k + 7);
+        w[k] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
       }
       *reinterpret_cast<u32x4*>(codes + t * (K / 2) + (int64_t)j * 16) = u32x4{w[0], w[1], w[2], w[3]};
     } else {
       uint32_t w[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        uint32_t d = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d |= (q[4 * k + i] & 0xFFu) << (8 * i);
-        w[k] = d;
-      }
+      for (int k = 0; k < 8; ++k) w[k] = low_bytes(4 * k, 4 * k + 1, 4 * k + 2, 4 * k + 3);
       u32x4* dst = reinterpret_cast<u32x4*>(codes + t * K + (int64_t)j * 32);
       dst[0] = u32x4{w[0], w[1], w[2], w[3]};
       dst[1] = u32x4{w[4], w[5], w[6], w[7]};
