@@ -852,6 +852,10 @@ def main():
     # 100 untimed steps (about 0.1 s) bring the GPU clocks to their steady state; with 3,
     # the first timed steps still ran about 10 % slower
     ap.add_argument("--warmup", type=int, default=100)
+    # untimed steps run for at least this long before the W warm-up steps, whatever W is:
+    # with 5 warm-up steps alone the dominant kernel measured 384 us against 361 us settled
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="minimum wall time of untimed steps before the warm-up steps")
     ap.add_argument("--workload", default="moe64s2_h2048_f1408")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefill-sample", type=int, default=256)
@@ -999,6 +1003,14 @@ def main():
     def run_step():
         run_mixed_step(torch, phases, side)
 
+    # clock settling: untimed steps for at least --settle-ms, checked once per 10 steps
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1000.0 < args.settle_ms:
+        for _ in range(10):
+            run_step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -1122,8 +1134,8 @@ def main():
     cfg["tables"] = args.tables
     cfg["index_layout"] = args.layout
     line = dict(metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps,
-                warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
-                scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,
+                warmup=args.warmup, settle_steps=settle_steps,
+                ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16", data="synthetic", config=cfg,
                 roofline=roofline, decode_roofline=decode_info, auto_path_step=auto_info,
                 cpu_baseline=cpu,
                 setup_s=round(setup_s, 1), host=platform.node())
