@@ -55,7 +55,8 @@ def test_rotate_quantize_explicit_blocks_and_stride(had_block):
 
 
 @pytest.mark.parametrize("K,had_block,act_bits", [(1056, 0, 4), (1088, 0, 8), (1408, 0, 4), (1536, 0, 8),
-                                                   (1984, 0, 4), (1408, 8, 8), (1408, 32, 4)])
+                                                   (1984, 0, 4), (1408, 8, 8), (1408, 32, 4),
+                                                   (1280, 0, 8), (1536, 256, 4), (1536, 64, 8)])
 def test_rotate_quantize_packed_tokens(K, had_block, act_bits):
     # K/32 lanes per token, not a power of two: tokens packed back to back in 512-lane
     # workgroups (8 to 15 tokens each), some of them straddling two waves; 50 tokens fill
@@ -66,6 +67,21 @@ def test_rotate_quantize_packed_tokens(K, had_block, act_bits):
     ref = oracle.rotate_quantize(np.ascontiguousarray(xb[:, :K]), had_block, act_bits)
     x = bf16_dev(xb)[:, :K]
     codes, scales = cbq.rotate_quantize(x, act_bits, had_block=had_block)
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+    assert np.array_equal(scales.cpu().numpy(), ref["scale"])
+
+
+@pytest.mark.parametrize("K,had_block,act_bits,T", [(1408, 0, 4, 9000), (1280, 0, 8, 9601),
+                                                     (1088, 0, 4, 12001)])
+def test_rotate_quantize_packed_tokens_looping(K, had_block, act_bits, T):
+    # enough token groups that each workgroup of the packed kernel loops over several
+    # (three workgroups per CU), loading the next group while working on the current one
+    # and rotating its absmax sets; T leaves the last group ragged
+    xb = datagen.random_tokens(K + T, T, K)
+    xb[T // 3] = 0
+    xb[-1] = 0
+    ref = oracle.rotate_quantize(xb, had_block, act_bits)
+    codes, scales = cbq.rotate_quantize(bf16_dev(xb), act_bits, had_block=had_block)
     assert np.array_equal(codes.cpu().numpy(), ref["codes"])
     assert np.array_equal(scales.cpu().numpy(), ref["scale"])
 
