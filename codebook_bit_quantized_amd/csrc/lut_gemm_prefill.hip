@@ -281,6 +281,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   __shared__ __attribute__((aligned(16))) uint32_t s_rowoff[BM];   // byte offset of each row in out
   __shared__ int64_t s_r0, s_me, s_m0, s_ttot;
   __shared__ uint32_t s_pad;
+  __shared__ uint64_t s_nruns;
   __shared__ int s_e;
 
   const int tid = threadIdx.x;
@@ -297,10 +298,12 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   // last run, have no work.  (The host makes the slots a multiple of 8 G' for a power of
   // two G' >= G and leaves room for a partial run per expert.)
   if (tid < 64) {
-    // the call's M-tiles, and the slots that runs of 2 and of 4 tiles would leave empty
-    // at the end of each expert (16-bit fields; they only steer the run length below)
+    // the call's M-tiles, the slots that runs of 2 and of 4 tiles would leave empty at
+    // the end of each expert (16-bit fields; they only steer the run length below), and
+    // the call's runs of 2 and of 4 tiles (32-bit fields)
     int64_t tot = 0;
     uint32_t pad = 0;
+    uint64_t nruns = 0;
     if (!offsets) {
       tot = n_rows > min_rows ? (n_rows + BM - 1) / BM : 0;
       pad = (uint32_t)((-tot) & 1) | ((uint32_t)((-tot) & 3) << 16);
@@ -311,16 +314,19 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
         if (ex < E) cnt = offsets[ex + 1] - offsets[ex];
         int64_t nt = cnt > min_rows ? (cnt + BM - 1) / BM : 0;
         uint32_t pd = (uint32_t)((-nt) & 1) | ((uint32_t)((-nt) & 3) << 16);
+        uint64_t nr = (uint64_t)((nt + 1) >> 1) | ((uint64_t)((nt + 3) >> 2) << 32);
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           nt += __shfl_xor(nt, d);
           pd += __shfl_xor(pd, d);
+          nr += __shfl_xor(nr, d);
         }
         tot += nt;
         pad += pd;
+        nruns += nr;
       }
     }
-    if (tid == 0) { s_ttot = tot; s_pad = pad; }
+    if (tid == 0) { s_ttot = tot; s_pad = pad; s_nruns = nruns; }
   }
   __syncthreads();
   const int64_t ttot = s_ttot;
@@ -334,7 +340,20 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
   const uint32_t q = (lin / 8) / gridDim.x;
   const uint32_t P = q / G;
-  const int64_t run = 8 * (int64_t)P + lin % 8, rr = q % G;   // run, tile of the run
+  const uint32_t x8 = lin % 8;                       // the XCD
+  int64_t run = 8 * (int64_t)P + x8;                 // run of this slot, before the exchange
+  const int64_t rr = q % G;                          // tile of the run
+  // Inside each whole block of 32 runs, XCD x takes runs 8 (x / 2) + (x mod 2) + 2a in its
+  // rounds a = 0..3 of the block, so the block's four aligned groups of 8 consecutive runs
+  // each stay on one pair of XCDs: an expert of 8 runs (the shared experts, which come
+  // first in the scan below) is fetched by two L2s instead of eight.  Slots past the
+  // last whole block keep the plain order, so every run of the call has a slot.
+  if (offsets) {
+    const uint64_t nr = s_nruns;
+    const int64_t runs = G == 1 ? ttot : G == 2 ? (int64_t)(uint32_t)nr : (int64_t)(nr >> 32);
+    if (run < runs / 32 * 32)
+      run = (run & ~(int64_t)31) + 8 * (x8 >> 1) + 2 * ((run >> 3) & 3) + (x8 & 1);
+  }
   const int tcol = (int)((lin / 8) % gridDim.x);
   // ---- (run, tile of the run) -> (expert, first row): wave 0 scans the experts' run counts ----
   if (tid < 64) {
@@ -348,9 +367,9 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
       if (tid == 0) s_e = -1;
       int64_t before = 0;                            // runs of earlier 64-expert chunks
       for (int base = 0; base < E; base += 64) {
-        const int ex = base + tid;
+        const int ex = E - 1 - (base + tid);         // the last experts (shared) first
         int64_t a = 0, cnt = 0;
-        if (ex < E) { a = offsets[ex]; cnt = offsets[ex + 1] - a; }
+        if (ex >= 0) { a = offsets[ex]; cnt = offsets[ex + 1] - a; }
         const int64_t nt = cnt > min_rows ? (cnt + BM - 1) / BM : 0;
         const int64_t nr = (nt + G - 1) / G;         // the expert's runs
         int64_t incl = nr;                           // inclusive scan over the wave
