@@ -354,8 +354,8 @@ __device__ __forceinline__ void swap_butterfly(double& a, double& b) {
 
 }  // namespace
 
-// Tokens of K/32 lanes (32 < K/32 < 64) packed back to back, Hadamard blocks of
-// b = 32 << g channels (0 <= g <= 4: b divides K < 2048).  A workgroup of 512 lanes holds 512 >> g blocks:
+// Tokens of K/32 >= 16 lanes packed back to back (at most 32 tokens a workgroup), Hadamard
+// blocks of b = 32 << g channels (0 <= g <= 6).  A workgroup of 512 lanes holds 512 >> g blocks:
 // block row r = lane mod (64 >> g) of each wave, and the block's 1 << g lanes are 64 >> g
 // lanes apart (jj = lane >> (6 - g) is the lane's place in its block), so the last one or
 // two lane stages of every block are at lane distances 16 and 32 and run as half-swaps:
@@ -449,6 +449,8 @@ rotate_quantize_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64
       }
     }
     // lane stages below distance 16 (g >= 3)
+    if constexpr (g >= 6) lane_stage<1>(v, (lane & 1) != 0);
+    if constexpr (g >= 5) lane_stage<2>(v, (lane & 2) != 0);
     if constexpr (g >= 4) lane_stage<4>(v, (lane & 4) != 0);
     if constexpr (g >= 3) lane_stage<8>(v, (lane & 8) != 0);
     // half-swaps: distance 16 with register bit 3, distance 32 with register bit 4
@@ -470,6 +472,8 @@ rotate_quantize_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64
       u[i] = (float)v[i];
       amax = fmaxf(amax, fabsf(u[i]));
     }
+    if constexpr (g >= 6) amax = fmaxf(amax, xor_lane_f32<1>(amax));
+    if constexpr (g >= 5) amax = fmaxf(amax, xor_lane_f32<2>(amax));
     if constexpr (g >= 4) amax = fmaxf(amax, xor_lane_f32<4>(amax));
     if constexpr (g >= 3) amax = fmaxf(amax, xor_lane_f32<8>(amax));
     if constexpr (g >= 2) amax = fmaxf(amax, xor_lane_f32<16>(amax));
@@ -544,8 +548,16 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
   int logb = 0;
   while ((1 << logb) < b) ++logb;
   const float c_b = (float)(1.0 / std::sqrt((double)b));
-  if (nthr > 32 && nthr < 64 && b >= 32 && smooth == nullptr && signs == nullptr &&
-      precond == nullptr) {
+  // Lanes of a 512-lane workgroup the packed kernel keeps busy, and the share of the
+  // general kernel's lanes that hold channels (G lanes per token, G a power of two up to
+  // 64, else whole waves).
+  const double packed_use = (double)(512 / nthr * nthr) / 512.0;
+  int g_lanes = 1;
+  while (g_lanes < nthr && g_lanes < 64) g_lanes <<= 1;
+  if (nthr > 64) g_lanes = (nthr + 63) / 64 * 64;
+  const double general_use = (double)nthr / g_lanes;
+  if (nthr >= 16 && b >= 32 && b <= 2048 && packed_use >= general_use && smooth == nullptr &&
+      signs == nullptr && precond == nullptr) {
     // packed tokens, plain rotation: groups of tpb tokens, each workgroup looping over
     // about the same number of groups.  Two workgroups are resident per CU (116 VGPRs);
     // a grid of three per CU measured fastest (32768 x 1408: 40.1 us warm, against 43.4
@@ -570,6 +582,8 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
       CBQ_RQ_PACKED(2)
       CBQ_RQ_PACKED(3)
       CBQ_RQ_PACKED(4)
+      CBQ_RQ_PACKED(5)
+      CBQ_RQ_PACKED(6)
       default: return hipErrorInvalidValue;
     }
 #undef CBQ_RQ_PACKED
