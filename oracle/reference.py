@@ -15,7 +15,7 @@ Sources (cited by page title and the section / figure on it):
   weight outliers are absorbed into cluster centroids, MoE models, dedicated LUT
   kernels); the AI Radio episode on the same paper (introduction: a router sends each
   input to an expert; "Improvements": the kernel precomputes products and looks them
-  up rather than recomputed; shared-memory bank conflicts).
+  up instead of recomputing them; shared-memory bank conflicts).
 
 Readings taken where the pages are silent (each is listed with its reason in the
 design notes of the repository):
