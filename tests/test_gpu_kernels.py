@@ -307,6 +307,9 @@ _RUN_CASES = {
     "mixed": {2: 1100, 10: 260, 30: 512, 65: 520, 70: 900, 79: 1024, 5: 90, 40: 70, 77: 100},
     # mostly one-tile experts: runs of one
     "short": {1: 1100, 66: 700, **{e: 40 + e for e in range(20, 60, 2)}},
+    # two experts of 4096 rows last (as shared experts are): scanned first, they fill the
+    # first block of 16 runs, whose groups of 8 runs stay on four XCDs; then a ragged tail
+    "shared": {3: 300, 12: 500, 40: 380, 66: 200, 78: 4096, 79: 4096},
 }
 
 
@@ -323,7 +326,7 @@ def test_prefill_run_placement(case, bits, act_bits, n_w, path):
     bm = 256 if bits == 4 else 128
     min_rows = cbq.AUTO_MAX_LUT_ROWS if path == cbq.PATH_AUTO else 0
     want_g = {("long", 128): 4, ("long", 256): 2, ("mixed", 128): 2, ("mixed", 256): 2,
-              ("short", 128): 1, ("short", 256): 1}[(case, bm)]
+              ("short", 128): 1, ("short", 256): 1, ("shared", 128): 4, ("shared", 256): 4}[(case, bm)]
     assert _prefill_run_length(counts, bm, min_rows) == want_g
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(offsets[-1])
