@@ -344,6 +344,7 @@ def bench_cpu_lut(args, cbq, torch):
     rate; beside it a bf16 GEMM of the dequantised weights (torch on the CPU: the dense
     model the method replaces) and the oracle."""
     import oracle
+    from codebook_bit_quantized_amd import allocation
     wl = datagen.WORKLOADS["dense2560x9728"]
     ws = datagen.dense_weights(wl, "gate_up")
     nbytes_w = ws.idx.nbytes + ws.codebook.nbytes
@@ -354,12 +355,15 @@ def bench_cpu_lut(args, cbq, torch):
         big.sum()
     stream_gbs = 5 * big.numel() * 4 / (time.perf_counter() - t0) / 1e9
     del big
-    W = torch.from_numpy(oracle.dequantize(oracle.unpack_indices(ws.idx[0], ws.K, ws.bits),
-                                           ws.codebook[0]).astype(np.float32)).to(torch.bfloat16)
+    W = torch.from_numpy(allocation.dequantize_rows(ws.idx[0], ws.codebook[0], ws.K, ws.bits)
+                         .astype(np.float32)).to(torch.bfloat16)
     rows = {}
     for T in wl.T_list:
         x = datagen.dense_tokens(wl, T)
-        rq = oracle.rotate_quantize(x, 0, wl.act_bits)
+        # the activation codes come from the library's rotate_quantize on the GPU
+        codes_d, scales_d = cbq.rotate_quantize(
+            torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16), wl.act_bits)
+        rq = dict(codes=codes_d.cpu().numpy(), scale=scales_d.cpu().numpy())
         out = np.empty((T, wl.N), dtype=np.float32)
         reps = max(5, args.steps)
         t_var = {}
@@ -372,7 +376,7 @@ def bench_cpu_lut(args, cbq, torch):
                                  out=out, avx512=wide)
             t_var[name] = (time.perf_counter() - t0) / reps
         t_lut = t_var["avx512"]
-        xb = torch.from_numpy(oracle.bf16_bits_to_f64(x).astype(np.float32)).to(torch.bfloat16)
+        xb = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
         torch.matmul(xb, W.t())
         t0 = time.perf_counter()
         for _ in range(reps):
@@ -510,6 +514,7 @@ def bench_kmeans(args, cbq, torch):
     rows in and the codebooks out at HBM bandwidth (the kernel is bound by its
     sort and its dependent search steps, well short of that)."""
     import oracle
+    from codebook_bit_quantized_amd import allocation
     wl = datagen.WORKLOADS[args.workload]
     dev = "cuda:0"
     R, K, bits = (wl.E + wl.n_shared) * wl.F, wl.H, wl.bits_gate_up
@@ -541,7 +546,7 @@ def bench_kmeans(args, cbq, torch):
         cpu = dict(value=n / dt, unit="rows/s", cores=1, kind="oracle",
                    sample=f"oracle per-row K-means on the first {n} rows ({dt:.1f} s, numpy fp64)")
     # output-aware refit on 128 calibration tokens of the layer input; its effect on the
-    # output error is measured by the oracle on held-out tokens for a sample of rows
+    # output error is measured on held-out tokens for a sample of rows
     n_cal = 128
     xc_np = datagen.activations_bf16(wl.wid, datagen.TAG_X_DECODE, n_cal, K)
     xt_np = datagen.activations_bf16(wl.wid + 1, datagen.TAG_X_DECODE, n_cal, K)
@@ -558,11 +563,11 @@ def bench_kmeans(args, cbq, torch):
         rtimes.append(s.elapsed_time(e) / 1000.0)
     tr = float(np.median(rtimes))
     rows = np.arange(0, R, max(1, R // 256))[:256]
-    idx_np = oracle.unpack_indices(cw.idx.cpu().numpy().reshape(R, -1)[rows], K, bits)
+    idx_np = cw.idx.cpu().numpy().reshape(R, -1)[rows]
     cb_before = cb0.cpu().numpy().reshape(R, -1)[rows].view(np.uint16)
     cb_after = cw.codebook.cpu().numpy().reshape(R, -1)[rows].view(np.uint16)
-    err0 = oracle.output_error(w_np[rows], idx_np, cb_before, xt_np)
-    err1 = oracle.output_error(w_np[rows], idx_np, cb_after, xt_np)
+    err0 = allocation.output_error(w_np[rows], idx_np, cb_before, xt_np, K, bits)
+    err1 = allocation.output_error(w_np[rows], idx_np, cb_after, xt_np, K, bits)
     refit = dict(rows_per_s=round(R / tr, 1), ms=round(tr * 1000.0, 3), calibration_tokens=n_cal,
                  held_out_output_error_kmeans=round(err0, 5), held_out_output_error_refit=round(err1, 5),
                  sample_rows=int(len(rows)))

@@ -91,6 +91,26 @@ def f16_bits_to_float(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float64)
 
 
+def dequantize_rows(idx_packed: np.ndarray, codebook_bits: np.ndarray, K: int, bits: int) -> np.ndarray:
+    """The weights [R][K] (float64) a clustered matrix stands for: row r's centroid at each
+    of its K indices (idx_packed [R][K*bits/8] as the cbq_weights bitstream, codebook_bits
+    [R][2^bits] fp16 patterns)."""
+    idx = unpack_indices(idx_packed, K, bits)
+    cb = f16_bits_to_float(np.asarray(codebook_bits).reshape(idx.shape[0], -1))
+    return np.take_along_axis(cb, idx, axis=1)
+
+
+def output_error(w_bits: np.ndarray, idx_packed: np.ndarray, codebook_bits: np.ndarray,
+                 x_bits: np.ndarray, K: int, bits: int) -> float:
+    """Relative error of a clustered matrix on the layer output: ||X (W - W')^T||_F /
+    ||X W^T||_F for tokens X [n][K] (bf16 patterns), rows W [R][K] (bf16 patterns) and their
+    clustering W' (CodeQuant2, Figure 3 right: the centroids are refit to the output error)."""
+    W = bf16_bits_to_float(w_bits)
+    Wc = dequantize_rows(idx_packed, codebook_bits, K, bits)
+    X = bf16_bits_to_float(x_bits)
+    return float(np.linalg.norm(X @ (W - Wc).T) / np.linalg.norm(X @ W.T))
+
+
 def expert_share(offsets: np.ndarray, T: int, n_routed: int, n_shared: int) -> np.ndarray:
     """Importance proxy per expert from the router's row offsets [E + S + 1]: the share of
     the T tokens routed to each of the E routed experts, and 1 for each shared expert

@@ -6,6 +6,8 @@ import itertools
 import numpy as np
 import pytest
 
+import oracle
+from codebook_bit_quantized_amd import allocation
 from codebook_bit_quantized_amd.allocation import allocate_bits
 
 
@@ -85,3 +87,26 @@ def test_expert_share_from_offsets():
     share = expert_share(rt["offsets"], 40, 8, 1)
     assert np.array_equal(share[:8], rt["counts"] / 40.0)
     assert share[8] == 1.0 and share[:8].sum() == 2.0   # top-2: every token counted twice
+
+
+def test_dequantize_rows_and_output_error_match_the_oracle():
+    # the allocation module's own decoding (used by the benchmark's quality figures) against
+    # the oracle's definitions, on random packed rows of every width
+    rng = np.random.default_rng(11)
+    for bits in (2, 3, 4):
+        R, K, n = 6, 96, 5
+        idx = rng.integers(0, 1 << bits, (R, K))
+        packed = np.zeros((R, K * bits // 8), dtype=np.uint8)
+        for r in range(R):
+            v = 0
+            for k in range(K):
+                v |= int(idx[r, k]) << (k * bits)
+            packed[r] = np.frombuffer(v.to_bytes(K * bits // 8, "little"), dtype=np.uint8)
+        cb = rng.standard_normal((R, 1 << bits)).astype(np.float16).view(np.uint16)
+        w = (rng.standard_normal((R, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        x = (rng.standard_normal((n, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        want_w = oracle.dequantize(oracle.unpack_indices(packed, K, bits), cb)
+        assert np.array_equal(allocation.dequantize_rows(packed, cb, K, bits), want_w)
+        got = allocation.output_error(w, packed, cb, x, K, bits)
+        want = oracle.output_error(w, oracle.unpack_indices(packed, K, bits), cb, x)
+        assert abs(got - want) <= 1e-12 * max(1.0, want)
