@@ -625,6 +625,22 @@ def bench_peaks(args, torch):
         us = cold_us(torch, flush, lambda: torch.sum(buf, dim=0, out=out[0]), 30)
         cold[name] = dict(bytes=nbytes, us=round(us, 2), GBs=round(nbytes / us / 1e3, 1))
         del buf
+    # the same decode GEMMs on uncompressed bf16 weights (the model the method replaces),
+    # cold, through the library GEMM: the headline decode gate/up's 65 active experts (gate
+    # and up side by side, 8 rows each, one batched GEMM) and the dense 2560 -> 9728 linear
+    # at T = 16; both operands contiguous
+    torch.manual_seed(0)
+    bf16_decode = {}
+    for name, E_, M, K, N in (("moe64s2_gate_up_65_experts", 65, 8, 2048, 2 * 1408),
+                              ("dense_2560x9728_T16", 1, 16, 2560, 9728)):
+        x = torch.randn(E_, M, K, device=dev).to(torch.bfloat16)
+        w = (torch.randn(E_, K, N, device=dev) * 0.02).to(torch.bfloat16)
+        o = torch.empty(E_, M, N, device=dev, dtype=torch.bfloat16)
+        us = cold_us(torch, flush, lambda: torch.bmm(x, w, out=o), 20)
+        wbytes = E_ * K * N * 2
+        bf16_decode[name] = dict(experts=E_, rows=M, K=K, N=N, weight_bytes=wbytes, us=round(us, 2),
+                                 GBs=round(wbytes / us / 1e3, 1))
+        del x, w, o
     del flush
 
     gemms = {}
@@ -641,7 +657,8 @@ def bench_peaks(args, torch):
             gemms[f"{dt_name}_{name}"] = dict(M=M, K=K, N=N, us=round(ms * 1000, 1),
                                                TFLOPs=round(2 * M * K * N / (ms / 1000) / 1e12, 1))
             del a, b
-    line = dict(mode="peaks", hbm=hbm, cold=cold, hbm_vendor_GBs=HBM_PEAK_GBS,
+    line = dict(mode="peaks", hbm=hbm, cold=cold, bf16_decode_cold=bf16_decode,
+                hbm_vendor_GBs=HBM_PEAK_GBS,
                 hbm_copy_frac_of_vendor=round(hbm["copy_GBs"] / HBM_PEAK_GBS, 3),
                 hbm_read_frac_of_vendor=round(hbm["read_GBs"] / HBM_PEAK_GBS, 3),
                 gemm=gemms, mfma_vendor_TFLOPs=F16_MFMA_PEAK_TFLOPS,
