@@ -156,6 +156,9 @@ class MoEPhase:
         self.scales_h = torch.empty((self.R,), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.R, H), dtype=torch.float32, device=dev)
         self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        # the down GEMM's optional workspace (a K split when its tiles would leave CUs idle)
+        nws = cbq.gemm_workspace([W["down"]], self.R, a, cbq.PATH_AUTO)
+        self.ws_dn = torch.empty((nws,), dtype=torch.uint8, device=dev) if nws > 0 else None
         self.path_gu, self.path_dn = path_gu, path_dn
         self.ev = None   # (start, end) events around the gate/up GEMM when timing it
 
@@ -177,7 +180,7 @@ class MoEPhase:
         cbq.rotate_quantize(self.h, a, codes=self.codes_h, scales=self.scales_h, stream=stream)
         cbq.codebook_lut_gemm(self.codes_h, self.scales_h, a, [W["down"]], n_rows=self.R,
                               expert_offsets=self.rt["offsets"], path=self.path_dn, out=self.out,
-                              stream=stream)
+                              ws=self.ws_dn, stream=stream)
         cbq.moe_combine(self.out, self.rt["slot_of"], self.rt["weights"], wl.n_shared, y=self.y,
                         stream=stream)
 
@@ -192,7 +195,7 @@ class MoEPhase:
     def gemm_dn_only(self):
         self.cbq.codebook_lut_gemm(self.codes_h, self.scales_h, self.wl.act_bits, [self.W["down"]],
                                    n_rows=self.R, expert_offsets=self.rt["offsets"],
-                                   path=self.path_dn, out=self.out)
+                                   path=self.path_dn, out=self.out, ws=self.ws_dn)
 
 
 def run_mixed_step(torch, phases, side=None):

@@ -19,12 +19,12 @@ from ._binding import (AUTO_MAX_LUT_ROWS, CBQ_EHIP, CBQ_EINVAL, CBQ_EUNSUPPORTED
                        moe_route_gather_noalloc, prepack_weights, LAYOUT_ROWS, LAYOUT_BLOCKED,
                        refit_codebooks,
                        rotate_dense_workspace, rotate_quantize, rotate_quantize_dense,
-                       route_workspace)
+                       route_workspace, gemm_workspace)
 
 __all__ = [
     "rotate_quantize", "moe_route_gather", "moe_route_gather_noalloc", "prepack_weights", "LAYOUT_ROWS", "LAYOUT_BLOCKED",
     "codebook_lut_gemm", "moe_combine", "moe_ffn",
-    "route_workspace", "kmeans_codebooks", "refit_codebooks", "cpu_lut_gemm", "rotate_quantize_dense",
+    "route_workspace", "gemm_workspace", "kmeans_codebooks", "refit_codebooks", "cpu_lut_gemm", "rotate_quantize_dense",
     "rotate_dense_workspace",
     "CodebookWeights", "CbqError", "load_library", "LIB_PATH", "EXPORTED", "cbq_weights",
     "EPI_F32", "EPI_SWIGLU_BF16", "PATH_AUTO", "PATH_LUT", "PATH_MFMA", "PATH_PAGES_PRODUCTS", "PATH_PAGES_BUCKETS", "PATH_REG_TABLES", "PATH_LDS_TABLES", "AUTO_MAX_LUT_ROWS",

@@ -276,14 +276,25 @@ def prepack_weights(w: CodebookWeights, stream=None) -> CodebookWeights:
     return CodebookWeights(idx=dst, codebook=w.codebook, K=w.K, bits=w.bits, layout=LAYOUT_BLOCKED)
 
 
+def gemm_workspace(weights: Sequence[CodebookWeights], n_rows: int, act_bits: int,
+                   path: int = PATH_AUTO) -> int:
+    """Bytes of optional GEMM workspace (cbq_gemm_workspace): with it, a single-matrix MFMA
+    call whose tiles would leave CUs idle splits K in two; 0 when no call of these sizes can."""
+    arr = (cbq_weights * len(weights))(*[w.c_struct() for w in weights])
+    return int(load_library().cbq_gemm_workspace(arr, len(weights), n_rows, act_bits, path))
+
+
 def codebook_lut_gemm(codes: torch.Tensor, scales: torch.Tensor, act_bits: int,
                       weights: Sequence[CodebookWeights], n_rows: Optional[int] = None,
                       expert_offsets: Optional[torch.Tensor] = None,
                       row_token: Optional[torch.Tensor] = None, epilogue: Optional[int] = None,
-                      path: int = PATH_AUTO, out: Optional[torch.Tensor] = None, stream=None):
-    """Grouped codebook GEMM.  One weight set -> fp32 [R][N]; {gate, up} -> bf16 SwiGLU [R][N]."""
+                      path: int = PATH_AUTO, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    """Grouped codebook GEMM.  One weight set -> fp32 [R][N]; {gate, up} -> bf16 SwiGLU [R][N].
+
+    ws: optional device workspace (a tensor of gemm_workspace(...) bytes or more)."""
     lib = load_library()
-    _require_gpu(codes, scales, expert_offsets, row_token)
+    _require_gpu(codes, scales, expert_offsets, row_token, ws)
     n_w = len(weights)
     if epilogue is None:
         epilogue = EPI_SWIGLU_BF16 if n_w == 2 else EPI_F32
@@ -296,7 +307,9 @@ def codebook_lut_gemm(codes: torch.Tensor, scales: torch.Tensor, act_bits: int,
     arr = (cbq_weights * n_w)(*[w.c_struct() for w in weights])
     _check(lib.cbq_codebook_lut_gemm(_ptr(codes), _ptr(scales), act_bits, n_rows,
                                      _ptr(expert_offsets), _ptr(row_token), arr, n_w, epilogue,
-                                     path, _ptr(out), out.stride(0), None, 0, _stream(stream)))
+                                     path, _ptr(out), out.stride(0), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)))
     return out
 
 

@@ -204,8 +204,11 @@ CBQ_EXPORT int cbq_prepack_weights(const cbq_weights* src, uint8_t* dst, void* s
 
 CBQ_EXPORT size_t cbq_gemm_workspace(const cbq_weights* W, int32_t n_w, int64_t n_rows,
                                      int32_t act_bits, int32_t path) {
-  (void)W; (void)n_w; (void)n_rows; (void)act_bits; (void)path;
-  return 0;
+  (void)act_bits;
+  if (!W || (n_w != 1 && n_w != 2)) return 0;
+  const int p = path & ~(CBQ_PATH_REG_TABLES | CBQ_PATH_LDS_TABLES);
+  if (p != CBQ_PATH_AUTO && p != CBQ_PATH_MFMA) return 0;   // only the MFMA path uses it
+  return cbq::mfma_split_workspace_bytes(n_w, W[0].bits, n_rows, W[0].N, W[0].K);
 }
 
 CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, int32_t act_bits,
@@ -214,7 +217,6 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
                                      int32_t epilogue, int32_t path, void* out, int64_t ldo,
                                      void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  (void)ws; (void)ws_bytes;
   if (!W) return fail(CBQ_EINVAL, "W must be non-null");
   if (n_w != 1 && n_w != 2) return fail(CBQ_EINVAL, "n_w must be 1 or 2 (got %d)", n_w);
   for (int i = 0; i < n_w; ++i) {
@@ -259,8 +261,11 @@ CBQ_EXPORT int cbq_codebook_lut_gemm(const uint8_t* codes, const float* scales, 
   }
   if (!codes || !scales || !out) return fail(CBQ_EINVAL, "codes, scales and out must be non-null");
   if (!aligned16(codes) || !aligned16(out)) return fail(CBQ_EINVAL, "codes and out must be 16-byte aligned");
+  if (ws && ws_bytes > 0 && !aligned16(ws)) return fail(CBQ_EINVAL, "ws must be 16-byte aligned");
 
   cbq::GemmArgs a{};
+  a.ws = ws_bytes > 0 ? ws : nullptr;
+  a.ws_bytes = a.ws ? ws_bytes : 0;
   a.codes = codes; a.scales = scales; a.act_bits = act_bits; a.n_rows = n_rows;
   a.offsets = expert_offsets; a.row_token = row_token;
   a.w[0] = cbq::GemmW{W[0].idx, W[0].codebook};

@@ -34,6 +34,8 @@ struct GemmArgs {
   int blocked;              // 1: indices in the blocked layout (cbq_prepack_weights)
   void* out;
   int64_t ldo;
+  void* ws;                 // optional workspace (K-split partial sums of the MFMA path)
+  size_t ws_bytes;
 };
 
 hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t ldx, int b,
@@ -55,6 +57,11 @@ hipError_t launch_lut_decode(const GemmArgs& a, int max_rows, hipStream_t stream
 
 // MFMA (prefill) path.  Experts with at most min_rows rows are skipped (AUTO split).
 hipError_t launch_mfma_prefill(const GemmArgs& a, int min_rows, hipStream_t stream);
+
+// Workspace bytes with which a single-matrix MFMA call of these sizes may split K in two
+// (0: it never splits).  The launcher splits when the workspace holds that many bytes and
+// the call's 256-row tiles would leave CUs idle.
+size_t mfma_split_workspace_bytes(int n_w, int bits, int64_t n_rows, int N, int K);
 
 // The pages' table forms (4-bit codebooks, A4): mode 0 per-row product tables with sign
 // folding, mode 1 per-row integer buckets of the activation codes.

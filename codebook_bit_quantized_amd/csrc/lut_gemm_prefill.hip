@@ -272,7 +272,9 @@ __global__ void __launch_bounds__(256, (BM == 128 || NS == 1) ? 2 : 1)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
-                    int blocked, void* __restrict__ out, int64_t ldo) {
+                    int blocked, void* __restrict__ out, int64_t ldo, float* __restrict__ ws) {
+  // K split z of gridDim.z (single matrix only): z = 0 writes out, z >= 1 writes its
+  // partial sums to ws + (z - 1) * n_rows * N (pitch N); a reduction adds them after.
   // LDS pair tables: per wave, two matrix slots of 32 rows, NE entries each
   constexpr int NE = LT ? PairTab<BITS>::NE : 1;
   __shared__ __attribute__((aligned(16))) uint32_t Tab[LT ? 4 * 2 * NE * 32 : 1];
@@ -396,9 +398,16 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const int64_t r0 = s_r0, me = s_me, m0 = s_m0;
   const int rows = (int)((me - m0) < BM ? (me - m0) : BM);
   const int nms = (rows + 31) >> 5;                  // 32-row sub-tiles holding rows
+  // this split's channels [k0, k0 + Kl): whole 64-channel steps, the last split takes the tail
+  const int nsplit = (int)gridDim.z, split = (int)blockIdx.z;
+  const int sps = ((K + BK - 1) / BK + nsplit - 1) / nsplit;
+  const int k0 = split * sps * BK;
+  const int Kl = K - k0 < sps * BK ? K - k0 : sps * BK;
+  if (Kl <= 0) return;                               // uniform over the workgroup
+  const int64_t pitch = split == 0 ? ldo : (int64_t)N;
 
   TileCtx<BITS, ABITS, LT> c;
-  c.K = K;
+  c.K = Kl;
   c.tid = tid;
   c.rows = rows;
   // ---- activation loader: threads 2i and 2i + 1 own the two 32-code halves of tile row i ----
@@ -413,7 +422,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
       const int64_t r = r0 + m0 + tid;
       const int64_t tk = row_token ? (int64_t)row_token[r] : r;
       sv = scales[tk];
-      ro = (uint32_t)(r * ldo * ESZ);
+      ro = (uint32_t)(r * pitch * ESZ);
     }
     s_rowoff[tid] = ro;
     s_scale[tid] = sv;
@@ -423,7 +432,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
     atok = row_token ? (int64_t)row_token[r] : r;
   }
   c.cres = make_rsrc(codes, 0x7FFFFFFFu);
-  c.crow_off = (uint32_t)(atok * ((int64_t)K * ABITS / 8));
+  c.crow_off = (uint32_t)(atok * ((int64_t)K * ABITS / 8) + (int64_t)k0 * ABITS / 8);
 
   // ---- weight rows of this lane ----
   const int lane = tid & 63, wave = tid >> 6;
@@ -460,12 +469,16 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
     }
     c.wres[s] = make_rsrc(W.idx + (int64_t)e * N * row_bytes, (uint32_t)(N * row_bytes));
     const int nr = c.nvalid[s] ? c.nrow[s] : 0;
-    c.wrow_off[s] = blocked ? (uint32_t)((nr & ~15) * row_bytes) + (uint32_t)((c.g * 16 + (nr & 15)) * 4 * BITS)
-                            : (uint32_t)(nr * row_bytes) + (uint32_t)(c.g * 4 * BITS);
+    c.wrow_off[s] = (blocked ? (uint32_t)((nr & ~15) * row_bytes) + (uint32_t)((c.g * 16 + (nr & 15)) * 4 * BITS)
+                             : (uint32_t)(nr * row_bytes) + (uint32_t)(c.g * 4 * BITS)) +
+                    (uint32_t)(k0 / BK) * c.wstep;
   }
 
-  // output buffer: every row of this call (n_rows) x ldo elements
-  const __amdgpu_buffer_rsrc_t ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
+  // output buffer: every row of this call (n_rows) x ldo elements, or this split's slice
+  // of the partial sums (n_rows x N)
+  const __amdgpu_buffer_rsrc_t ores =
+      split == 0 ? make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ))
+                 : make_rsrc(ws + (int64_t)(split - 1) * n_rows * N, (uint32_t)(n_rows * N * 4));
   switch (nms) {
     case 1: tile_run<BITS, ABITS, NW, 1, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
     case 2: tile_run<BITS, ABITS, NW, 2, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
@@ -482,6 +495,38 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
       }
       break;
   }
+}
+
+// Adds the partial sums of K splits 1 .. nsplit-1 (ws, pitch N) to split 0's rows in out,
+// in split order, for the rows the MFMA path computed: rows of experts with more than
+// min_rows rows.  One row per workgroup pass.
+__global__ void __launch_bounds__(256)
+mfma_split_reduce_kernel(float* __restrict__ out, int64_t ldo, const float* __restrict__ ws,
+                         int nsplit, int64_t n_rows, int N, const int32_t* __restrict__ offsets,
+                         int E, int min_rows) {
+  for (int64_t r = blockIdx.x; r < n_rows; r += gridDim.x) {
+    if (offsets) {
+      // the expert holding row r: the last e with offsets[e] <= r
+      int lo = 0, hi = E;                            // offsets[lo] <= r < offsets[hi] if inside
+      if (r < offsets[0] || r >= offsets[E]) continue;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= r) lo = mid; else hi = mid;
+      }
+      if (offsets[lo + 1] - offsets[lo] <= min_rows) continue;
+    }
+    float* o = out + r * ldo;
+    for (int n = threadIdx.x; n < N; n += blockDim.x) {
+      float v = o[n];
+      for (int s = 1; s < nsplit; ++s) v += ws[((int64_t)(s - 1) * n_rows + r) * N + n];
+      o[n] = v;
+    }
+  }
+}
+
+size_t mfma_split_workspace_bytes(int n_w, int bits, int64_t n_rows, int N, int K) {
+  if (n_w != 1 || bits != 4 || K < 4096 || n_rows <= 0) return 0;
+  return (size_t)n_rows * (size_t)N * sizeof(float);
 }
 
 template <int BITS, int ABITS, bool LT, bool BLK>
@@ -504,22 +549,37 @@ static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream)
   if (a.n_w == 2) {
     hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK, 2>), grid_for(128), dim3(256), 0, stream,
                        a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                       min_rows, a.blocked, a.out, a.ldo);
+                       min_rows, a.blocked, a.out, a.ldo, nullptr);
     return hipGetLastError();
   }
   if constexpr (BM == 256) {
     // a single matrix whose 256-column tiles would leave CUs idle (fewer than two
-    // workgroups per CU even with every M-tile slot filled) takes 128-column tiles
+    // workgroups per CU even with every M-tile slot filled) takes 128-column tiles; with
+    // a workspace it also splits K in two, so both workgroup slots of each CU fill, and
+    // adds the second half's partial sums in a second, ordered pass
     if ((int64_t)((a.N + 255) / 256) * mt < 2 * 256) {
-      hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 1>), grid_for(128), dim3(256), 0, stream,
+      const size_t need = mfma_split_workspace_bytes(a.n_w, BITS, a.n_rows, a.N, a.K);
+      const int nsplit = (need > 0 && a.ws != nullptr && a.ws_bytes >= need &&
+                          (int64_t)((a.N + 127) / 128) * mt < 2 * 256) ? 2 : 1;
+      dim3 grid = grid_for(128);
+      grid.z = (unsigned)nsplit;
+      hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 1>), grid, dim3(256), 0, stream,
                          a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                         min_rows, a.blocked, a.out, a.ldo);
+                         min_rows, a.blocked, a.out, a.ldo, static_cast<float*>(a.ws));
+      if (nsplit > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const unsigned blocks = (unsigned)(a.n_rows < 4096 ? a.n_rows : 4096);
+        hipLaunchKernelGGL(mfma_split_reduce_kernel, dim3(blocks), dim3(256), 0, stream,
+                           static_cast<float*>(a.out), a.ldo, static_cast<const float*>(a.ws), nsplit,
+                           a.n_rows, a.N, a.offsets, E, min_rows);
+      }
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 2>), grid_for(256), dim3(256), 0, stream,
                      a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                     min_rows, a.blocked, a.out, a.ldo);
+                     min_rows, a.blocked, a.out, a.ldo, nullptr);
   return hipGetLastError();
 }
 

@@ -177,6 +177,19 @@ def test_gemm_validation():
     assert _gemm(lib, [_w()], codes=0x4004) == E                  # misaligned codes
     assert _gemm(lib, [_w()], n_rows=0) == cbq.CBQ_OK             # empty: no-op
     assert lib.cbq_gemm_workspace(ctypes.pointer(_w()), 1, 16, 4, 0) == 0
+    # the K-split workspace: one 4-bit matrix with K >= 4096 on the AUTO or MFMA path only
+    w4k = _w(K=4096)
+    assert lib.cbq_gemm_workspace(ctypes.pointer(w4k), 1, 16, 4, cbq.PATH_AUTO) == 16 * 64 * 4
+    assert lib.cbq_gemm_workspace(ctypes.pointer(w4k), 1, 16, 8, cbq.PATH_MFMA | cbq.PATH_REG_TABLES) == 16 * 64 * 4
+    assert lib.cbq_gemm_workspace(ctypes.pointer(w4k), 1, 16, 4, cbq.PATH_LUT) == 0
+    assert lib.cbq_gemm_workspace(ctypes.pointer(w4k), 1, 16, 4, cbq.PATH_PAGES_PRODUCTS) == 0
+    assert lib.cbq_gemm_workspace(ctypes.pointer(_w(K=4096, bits=3)), 1, 16, 4, cbq.PATH_AUTO) == 0
+    pair = (cbq.cbq_weights * 2)(w4k, w4k)
+    assert lib.cbq_gemm_workspace(pair, 2, 16, 4, cbq.PATH_AUTO) == 0     # SwiGLU pair: never split
+    arr = (cbq.cbq_weights * 1)(w4k)
+    assert lib.cbq_codebook_lut_gemm(ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000), 4, 16, None, None,
+                                     arr, 1, 0, 0, ctypes.c_void_p(0x3000), 64, ctypes.c_void_p(0x6004),
+                                     4096, None) == E               # misaligned workspace
     assert _gemm(lib, [_w(layout=2)]) == E                        # unknown layout
     assert _gemm(lib, [_w(), _w(layout=1)], n_w=2, epi=1) == E    # gate/up layouts differ
     assert _gemm(lib, [_w(layout=1)], n_rows=0) == cbq.CBQ_OK

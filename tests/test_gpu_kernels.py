@@ -400,3 +400,50 @@ def test_combine(T, k, S, H):
     ref = oracle.combine(out, slot, rt["weights"], T, k, S)
     y = cbq.moe_combine(to_dev(out), to_dev(slot), to_dev(rt["weights"]), S)
     assert_normwise(y.cpu().numpy(), ref, 1e-5, "combine")
+
+
+@pytest.mark.parametrize("act_bits,K,path,dense", [(8, 4096, cbq.PATH_MFMA, False),
+                                                   (4, 4160, cbq.PATH_AUTO, False),
+                                                   (8, 4160, cbq.PATH_MFMA, True)])
+def test_mfma_split_k_workspace(act_bits, K, path, dense):
+    """A single 4-bit matrix with K >= 4096 whose 256-row tiles would leave CUs idle splits
+    K in two when given the workspace cbq_gemm_workspace asks for: the second half's partial
+    sums go to the workspace and are added to out in a second, ordered pass.  The result
+    equals the unsplit call up to the fp32 summation order and the oracle within 1e-3;
+    rows of experts AUTO sends to the LUT path (at most 32 rows) are not touched by the
+    pass (bit-identical to the unsplit call).  K = 4160 leaves the second half a ragged
+    last step; the dense case has no expert offsets."""
+    E, N, T = (1, 384, 300) if dense else (8, 384, 500)
+    rng = np.random.default_rng(act_bits * 1000 + K + dense)
+    if dense:
+        counts = np.array([T])
+    else:
+        counts = np.array([140, 0, 17, 300, 129, 32, 260, 90])   # empty, LUT-sized and MFMA experts
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    row_token = None if dense else rng.integers(0, T, R).astype(np.int32)
+    rq = oracle.rotate_quantize(datagen.random_tokens(900 + act_bits, T, K), 0, act_bits)
+    ws_np = datagen.random_weights(910 + act_bits, E, N, K, 4, keep_raw=False)
+    W = upload_weights(ws_np)
+    need = cbq.gemm_workspace([W], R, act_bits, path)
+    assert need == R * N * 4
+    assert cbq.gemm_workspace([W], R, act_bits, cbq.PATH_LUT) == 0
+    kw = dict(expert_offsets=None if dense else to_dev(offsets),
+              row_token=None if dense else to_dev(row_token), path=path, n_rows=R)
+    args = (to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits, [W])
+    plain = cbq.codebook_lut_gemm(*args, **kw)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)      # stale contents
+    split = cbq.codebook_lut_gemm(*args, ws=ws, **kw)
+    split2 = cbq.codebook_lut_gemm(*args, ws=ws, **kw)                  # the workspace reused
+    torch.cuda.synchronize()
+    p, s, s2 = plain.cpu().numpy(), split.cpu().numpy(), split2.cpu().numpy()
+    assert np.array_equal(s, s2), "the split call is deterministic"
+    ref = oracle.expert_gemm(rq["q"], rq["scale"], row_token, None if dense else offsets,
+                             ws_np.idx, ws_np.codebook, K, 4)
+    assert_normwise(s, ref, 1e-3, "split")
+    assert_normwise(s, p, 1e-6, "split vs unsplit")
+    if path == cbq.PATH_AUTO:
+        lut_rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in range(E)
+                                   if 0 < counts[e] <= cbq.AUTO_MAX_LUT_ROWS])
+        assert np.array_equal(s[lut_rows], p[lut_rows])
+    assert not np.array_equal(s, p), "the split path ran (its sums differ in order)"
