@@ -398,13 +398,19 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   const int64_t r0 = s_r0, me = s_me, m0 = s_m0;
   const int rows = (int)((me - m0) < BM ? (me - m0) : BM);
   const int nms = (rows + 31) >> 5;                  // 32-row sub-tiles holding rows
-  // this split's channels [k0, k0 + Kl): whole 64-channel steps, the last split takes the tail
-  const int nsplit = (int)gridDim.z, split = (int)blockIdx.z;
-  const int sps = ((K + BK - 1) / BK + nsplit - 1) / nsplit;
-  const int k0 = split * sps * BK;
-  const int Kl = K - k0 < sps * BK ? K - k0 : sps * BK;
-  if (Kl <= 0) return;                               // uniform over the workgroup
-  const int64_t pitch = split == 0 ? ldo : (int64_t)N;
+  // this split's channels [k0, k0 + Kl): whole 64-channel steps, the last split takes the
+  // tail (single matrix only; the gate/up pair is never split, and its code keeps none of this)
+  int split = 0, k0 = 0, Kl = K;
+  int64_t pitch = ldo;
+  if constexpr (NW == 1) {
+    const int nsplit = (int)gridDim.z;
+    split = (int)blockIdx.z;
+    const int sps = ((K + BK - 1) / BK + nsplit - 1) / nsplit;
+    k0 = split * sps * BK;
+    Kl = K - k0 < sps * BK ? K - k0 : sps * BK;
+    if (Kl <= 0) return;                             // uniform over the workgroup
+    if (split > 0) pitch = N;
+  }
 
   TileCtx<BITS, ABITS, LT> c;
   c.K = Kl;
