@@ -355,7 +355,8 @@ __device__ __forceinline__ void swap_butterfly(double& a, double& b) {
 }  // namespace
 
 // Tokens of K/32 >= 16 lanes packed back to back (at most 32 tokens a workgroup), Hadamard
-// blocks of b = 32 << g channels (0 <= g <= 6).  A workgroup of 512 lanes holds 512 >> g blocks:
+// blocks of b = 32 << g channels (0 <= g <= 6).  A workgroup of W lanes (512, or a smaller
+// multiple of 64 that fits long tokens better) holds W >> g blocks:
 // block row r = lane mod (64 >> g) of each wave, and the block's 1 << g lanes are 64 >> g
 // lanes apart (jj = lane >> (6 - g) is the lane's place in its block), so the last one or
 // two lane stages of every block are at lane distances 16 and 32 and run as half-swaps:
@@ -388,7 +389,7 @@ rotate_quantize_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64
   const int bpt = K >> (5 + g);              // blocks per token
   const int bw = wave * rows + r;            // block within the workgroup
   const int lt = bw / bpt, bt = bw - lt * bpt;
-  const int tpb = (512 >> g) / bpt;          // tokens per group
+  const int tpb = ((int)blockDim.x >> g) / bpt;   // tokens per group
   const bool in_group = lt < tpb;
   // channel of register 8h + m (m < 8) inside the token: c0 + ch(h) + m
   int c0;
@@ -548,32 +549,41 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
   int logb = 0;
   while ((1 << logb) < b) ++logb;
   const float c_b = (float)(1.0 / std::sqrt((double)b));
-  // Lanes of a 512-lane workgroup the packed kernel keeps busy, and the share of the
-  // general kernel's lanes that hold channels (G lanes per token, G a power of two up to
-  // 64, else whole waves).
-  const double packed_use = (double)(512 / nthr * nthr) / 512.0;
+  // The packed kernel's workgroup: 512 lanes, or, where 512 would leave more than a tenth
+  // of them idle (one long token a workgroup), the multiple of 64 up to 512 that leaves the
+  // fewest idle; the share of its lanes that hold channels, against the general kernel's
+  // (G lanes per token, G a power of two up to 64, else whole waves).
+  auto use_of = [&](int w) { return (double)(w / nthr * nthr) / w; };
+  int wg = 512;
+  if (use_of(512) < 0.9)
+    for (int w = 448; w >= 64; w -= 64)
+      if (w >= nthr && use_of(w) > use_of(wg)) wg = w;
+  const double packed_use = use_of(wg);
   int g_lanes = 1;
   while (g_lanes < nthr && g_lanes < 64) g_lanes <<= 1;
   if (nthr > 64) g_lanes = (nthr + 63) / 64 * 64;
   const double general_use = (double)nthr / g_lanes;
-  if (nthr >= 16 && b >= 32 && b <= 2048 && packed_use >= general_use && smooth == nullptr &&
-      signs == nullptr && precond == nullptr) {
+  // (On equal use, workgroups of 320 lanes measured slower than the general kernel at
+  // K = 9728, those of 448 and 512 faster at K = 14336 and 2048.)
+  const bool packed = packed_use > general_use || (packed_use == general_use && wg >= 448);
+  if (nthr >= 16 && b >= 32 && b <= 2048 && packed && smooth == nullptr && signs == nullptr &&
+      precond == nullptr) {
     // packed tokens, plain rotation: groups of tpb tokens, each workgroup looping over
     // about the same number of groups.  Two workgroups are resident per CU (116 VGPRs);
     // a grid of three per CU measured fastest (32768 x 1408: 40.1 us warm, against 43.4
     // for two per CU and 42.5 for one group per workgroup)
     const int g = logb - 5;
-    const int64_t tpb = (512 >> g) / (K >> logb);
+    const int64_t tpb = (wg >> g) / (K >> logb);
     const int64_t n_groups = (T + tpb - 1) / tpb;
     int cus = 0;
     hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
-    const int64_t slots = 3 * (int64_t)cus;
+    const int64_t slots = (int64_t)(3 * 512 / wg) * cus;
     const int64_t per = (n_groups + slots - 1) / slots;
     const int64_t blocks = (n_groups + per - 1) / per;
 #define CBQ_RQ_PACKED(G_)                                                                      \
   case G_:                                                                                    \
-    hipLaunchKernelGGL(rotate_quantize_packed_kernel<G_>, dim3((unsigned)blocks), dim3(512), 0, \
+    hipLaunchKernelGGL(rotate_quantize_packed_kernel<G_>, dim3((unsigned)blocks), dim3(wg), 0, \
                        stream, x, ldx, T, K, act_bits, c_b, codes, scales, n_groups);         \
     break;
     switch (g) {

@@ -74,12 +74,14 @@ def test_rotate_quantize_packed_tokens(K, had_block, act_bits):
 @pytest.mark.parametrize("K,had_block,act_bits,T", [(1408, 0, 4, 9000), (1280, 0, 8, 9601),
                                                      (1088, 0, 4, 12001), (2048, 0, 4, 6200),
                                                      (2560, 0, 8, 4801), (768, 0, 4, 17000),
-                                                     (512, 0, 8, 24700), (2048, 1024, 4, 6199)])
+                                                     (512, 0, 8, 24700), (2048, 1024, 4, 6199),
+                                                     (14336, 0, 8, 1700), (9728, 0, 4, 2500)])
 def test_rotate_quantize_packed_tokens_looping(K, had_block, act_bits, T):
     # enough token groups that each workgroup of the packed kernel loops over several
     # (three workgroups per CU), loading the next group while working on the current one
     # and rotating its absmax sets; T leaves the last group ragged.  Blocks of 32 to 2048
-    # channels: half-swap stages only (b <= 128) or after one to four DPP stages
+    # channels: half-swap stages only (b <= 128) or after one to four DPP stages; K = 14336
+    # takes workgroups of 448 lanes (one token each), K = 9728 the general kernel
     xb = datagen.random_tokens(K + T, T, K)
     xb[T // 3] = 0
     xb[-1] = 0
