@@ -883,7 +883,7 @@ def main():
                     help="minimum wall time of untimed steps before the warm-up steps")
     ap.add_argument("--workload", default="moe64s2_h2048_f1408")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-prefill-sample", type=int, default=256)
+    ap.add_argument("--cpu-prefill-sample", type=int, default=4096)
     ap.add_argument("--decode-reps", type=int, default=20)
     ap.add_argument("--flush", choices=("read", "write"), default="read",
                     help="how caches are emptied before cold GEMM timings (see CacheFlush)")
