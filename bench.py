@@ -156,9 +156,11 @@ class MoEPhase:
         self.scales_h = torch.empty((self.R,), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.R, H), dtype=torch.float32, device=dev)
         self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
-        # the down GEMM's optional workspace (a K split when its tiles would leave CUs idle)
+        # the GEMMs' optional workspaces (K splits where their tiles would leave CUs idle)
         nws = cbq.gemm_workspace([W["down"]], self.R, a, cbq.PATH_AUTO)
         self.ws_dn = torch.empty((nws,), dtype=torch.uint8, device=dev) if nws > 0 else None
+        nws = cbq.gemm_workspace([W["gate"], W["up"]], self.R, a, cbq.PATH_AUTO)
+        self.ws_gu = torch.empty((nws,), dtype=torch.uint8, device=dev) if nws > 0 else None
         self.path_gu, self.path_dn = path_gu, path_dn
         self.ev = None   # (start, end) events around the gate/up GEMM when timing it
 
@@ -172,7 +174,7 @@ class MoEPhase:
         cbq.codebook_lut_gemm(self.codes, self.scales, a, [W["gate"], W["up"]],
                               n_rows=self.R, expert_offsets=self.rt["offsets"],
                               row_token=self.rt["sorted_tokens"], path=self.path_gu, out=self.h,
-                              stream=stream)
+                              ws=self.ws_gu, stream=stream)
         if self.ev is not None:
             self.ev[1].record()
         if after_gate_up is not None:
@@ -189,7 +191,7 @@ class MoEPhase:
                                    [self.W["gate"], self.W["up"]], n_rows=self.R,
                                    expert_offsets=self.rt["offsets"],
                                    row_token=self.rt["sorted_tokens"], path=self.path_gu,
-                                   out=self.h)
+                                   out=self.h, ws=self.ws_gu)
 
 
     def gemm_dn_only(self):

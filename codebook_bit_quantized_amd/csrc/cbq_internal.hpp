@@ -43,6 +43,9 @@ hipError_t launch_rotate_quantize(const uint16_t* x, int64_t T, int K, int64_t l
                                   uint8_t* codes, float* scales, uint32_t* precond,
                                   hipStream_t stream);
 
+// Compute units of the current device (cached per device after the first query).
+hipError_t device_cu_count(int* out);
+
 size_t route_workspace_bytes(int64_t T, int E);
 // The library's own route scratch (no allocation): its size, and its device address on
 // the current device (looked up on that device's first call).

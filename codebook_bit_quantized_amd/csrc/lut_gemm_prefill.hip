@@ -61,6 +61,10 @@ struct TileCtx {
   uint32_t trow[2];                 // dword of entry 0 of this lane's row in each table
   bool avalid;
   int K, g, nl, tid, rows;
+  // K split of the gate/up pair (4-bit tiles): the tile stores its unscaled fp32 sums of g
+  // and u at byte offset poff[s] (+ the row's offset) of the workspace instead of h
+  bool partial = false;
+  uint32_t poff[2];
 };
 
 // NS: 32-column weight slots per wave (2; 1 for a single matrix in 128-column tiles).
@@ -232,7 +236,14 @@ __device__ __forceinline__ void tile_run(const TileCtx<BITS, ABITS, LT>& c, uint
       const int m0 = ms * 32 + 8 * q + 4 * g;            // rows m0 .. m0+3 of this lane
       const u32x4 ro = *reinterpret_cast<const u32x4*>(&s_rowoff[m0]);
       const f32x4 sc = *reinterpret_cast<const f32x4*>(&s_scale[m0]);
-      if constexpr (NW == 2) {
+      bool part = false;
+      if constexpr (NW == 2 && BM == 256) part = c.partial;
+      if (part) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) buf_store_f32(ores, ro[j] + c.poff[s], acc[ms][s][4 * q + j]);
+      } else if constexpr (NW == 2) {
         // bf16 h of rows m0..m0+3; lanes nl and nl ^ 1 hold columns 2p and 2p + 1 of
         // the same rows, so each pair trades one value per two rows and stores whole
         // dwords: the even lane rows m0 + j, the odd lane rows m0 + j + 1 (j = 0, 2).
@@ -272,9 +283,15 @@ __global__ void __launch_bounds__(256, (BM == 128 || NS == 1) ? 2 : 1)
 mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
                     GemmW w0, GemmW w1, int64_t n_rows, int E, int N, int K, int min_rows,
-                    int blocked, void* __restrict__ out, int64_t ldo, float* __restrict__ ws) {
-  // K split z of gridDim.z (single matrix only): z = 0 writes out, z >= 1 writes its
-  // partial sums to ws + (z - 1) * n_rows * N (pitch N); a reduction adds them after.
+                    int blocked, void* __restrict__ out, int64_t ldo, float* __restrict__ ws,
+                    int tc0) {
+  // K split z of gridDim.z (single matrix): z = 0 writes out, z >= 1 writes its partial
+  // sums to ws + (z - 1) * n_rows * N (pitch N); a reduction adds them after.  The gate/up
+  // pair with 256-row tiles, tc0 >= 0: column tiles tcol >= tc0 split in two, in calls of at
+  // most 8 M-tiles (one per XCD) only; the grid has ncol - tc0 extra column tiles, right of
+  // the ncol real ones, for the second halves.  Both halves write their unscaled sums of g
+  // and u to ws, planes [half][g or u][n_rows][N - 128 tc0], and mfma_swiglu_reduce_kernel
+  // forms h from them.
   // LDS pair tables: per wave, two matrix slots of 32 rows, NE entries each
   constexpr int NE = LT ? PairTab<BITS>::NE : 1;
   __shared__ __attribute__((aligned(16))) uint32_t Tab[LT ? 4 * 2 * NE * 32 : 1];
@@ -358,7 +375,24 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
     if (run < runs / 16 * 16)
       run = (run & ~(int64_t)15) + 8 * (x8 >> 2) + 4 * ((run >> 3) & 1) + (x8 & 3);
   }
-  const int tcol = (int)((lin / 8) % gridDim.x);
+  int tcol = (int)((lin / 8) % gridDim.x);
+  // The gate/up pair's tail split: with at most 8 M-tiles each XCD holds at most one, and
+  // works through its column tiles in rounds of its CUs; the host picks tc0 so that the
+  // column tiles of the last, partly filled round split in K and fill it.  The second
+  // halves follow the first ones in the XCD's order, ahead of the slots with no work.
+  bool tsplit = false;
+  int half = 0;
+  if constexpr (NW == 2 && BM == 256) {
+    const int ncol = (N + 127) / 128;
+    if (tc0 >= 0 && tcol >= tc0) {
+      if (ttot > 8) {
+        if (tcol >= ncol) return;                    // no split: no second halves
+      } else {
+        tsplit = true;
+        if (tcol >= ncol) { half = 1; tcol -= ncol - tc0; }
+      }
+    }
+  }
   // ---- (run, tile of the run) -> (expert, first row): wave 0 scans the experts' run counts ----
   if (tid < 64) {
     if (!offsets) {
@@ -410,6 +444,13 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
     Kl = K - k0 < sps * BK ? K - k0 : sps * BK;
     if (Kl <= 0) return;                             // uniform over the workgroup
     if (split > 0) pitch = N;
+  } else if constexpr (BM == 256) {
+    if (tsplit) {                                    // two halves; the host splits K >= 2048 only
+      split = half;
+      const int sps = ((K + BK - 1) / BK + 1) / 2;
+      k0 = split * sps * BK;
+      Kl = K - k0 < sps * BK ? K - k0 : sps * BK;
+    }
   }
 
   TileCtx<BITS, ABITS, LT> c;
@@ -421,6 +462,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   c.avalid = arow < rows;
   int64_t atok = 0;
   constexpr uint32_t ESZ = NW == 2 ? 2 : 4;
+  const int64_t rowb = tsplit ? (int64_t)(N - tc0 * 128) * 4 : pitch * ESZ;   // bytes between rows
   if (tid < BM) {                                    // thread t < BM: row t's scale and output offset
     uint32_t ro = kOffNone;
     float sv = 0.0f;
@@ -428,7 +470,7 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
       const int64_t r = r0 + m0 + tid;
       const int64_t tk = row_token ? (int64_t)row_token[r] : r;
       sv = scales[tk];
-      ro = (uint32_t)(r * pitch * ESZ);
+      ro = (uint32_t)(r * rowb);
     }
     s_rowoff[tid] = ro;
     s_scale[tid] = sv;
@@ -481,10 +523,21 @@ mfma_prefill_kernel(const uint8_t* __restrict__ codes, const float* __restrict__
   }
 
   // output buffer: every row of this call (n_rows) x ldo elements, or this split's slice
-  // of the partial sums (n_rows x N)
-  const __amdgpu_buffer_rsrc_t ores =
-      split == 0 ? make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ))
-                 : make_rsrc(ws + (int64_t)(split - 1) * n_rows * N, (uint32_t)(n_rows * N * 4));
+  // of the partial sums (n_rows x N), or the gate/up pair's four partial planes
+  __amdgpu_buffer_rsrc_t ores;
+  if (tsplit) {
+    const int64_t plane = n_rows * (int64_t)(N - tc0 * 128) * 4;
+    ores = make_rsrc(ws, (uint32_t)(4 * plane));
+    c.partial = true;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      c.poff[s] = c.nvalid[s] ? (uint32_t)((2 * split + s) * plane + (int64_t)(c.nrow[s] - tc0 * 128) * 4)
+                              : kOffCol;
+  } else if (split == 0) {
+    ores = make_rsrc(out, (uint32_t)(n_rows * ldo * ESZ));
+  } else {
+    ores = make_rsrc(ws + (int64_t)(split - 1) * n_rows * N, (uint32_t)(n_rows * N * 4));
+  }
   switch (nms) {
     case 1: tile_run<BITS, ABITS, NW, 1, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
     case 2: tile_run<BITS, ABITS, NW, 2, LT, BLK, BM, NS>(c, As, s_scale, s_rowoff, ores); break;
@@ -530,9 +583,73 @@ mfma_split_reduce_kernel(float* __restrict__ out, int64_t ldo, const float* __re
   }
 }
 
+// h for the gate/up pair's split column tiles (columns c0 .. N-1): g and u are the sums of
+// both K halves' partials (lower half first), then scaled and passed through SwiGLU as in
+// the kernel's own epilogue.  Runs only where the kernel split, i.e. in calls of at most 8
+// M-tiles (counted again here from the offsets), and only on rows the MFMA path computed.
+__global__ void __launch_bounds__(256)
+mfma_swiglu_reduce_kernel(uint16_t* __restrict__ out, int64_t ldo, const float* __restrict__ ws,
+                          int64_t n_rows, int N, int c0, const float* __restrict__ scales,
+                          const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets,
+                          int E, int min_rows, int bm) {
+  __shared__ int64_t s_tot;
+  if (threadIdx.x < 64) {
+    int64_t tot = 0;
+    if (!offsets) {
+      tot = n_rows > min_rows ? (n_rows + bm - 1) / bm : 0;
+    } else {
+      for (int base = 0; base < E; base += 64) {
+        const int ex = base + (int)threadIdx.x;
+        const int64_t cnt = ex < E ? offsets[ex + 1] - offsets[ex] : 0;
+        int64_t nt = cnt > min_rows ? (cnt + bm - 1) / bm : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) nt += __shfl_xor(nt, d);
+        tot += nt;
+      }
+    }
+    if (threadIdx.x == 0) s_tot = tot;
+  }
+  __syncthreads();
+  if (s_tot > 8) return;
+  const int W = N - c0;
+  const int64_t plane = n_rows * (int64_t)W;
+  for (int64_t r = blockIdx.x; r < n_rows; r += gridDim.x) {
+    if (offsets) {
+      if (r < offsets[0] || r >= offsets[E]) continue;
+      int lo = 0, hi = E;                            // the expert holding row r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= r) lo = mid; else hi = mid;
+      }
+      if (offsets[lo + 1] - offsets[lo] <= min_rows) continue;
+    } else if (n_rows <= min_rows) {
+      return;
+    }
+    const int64_t tk = row_token ? (int64_t)row_token[r] : r;
+    const float sc = scales[tk];
+    const float* p = ws + r * W;
+    uint16_t* o = out + r * ldo + c0;
+    // four columns a thread: N is a multiple of 16 and c0 of 128, so W is a multiple of 4,
+    // the planes and rows start on 16-byte boundaries, and (ldo % 4 == 0) the four bf16 of
+    // h form one aligned 8-byte store
+    for (int n = 4 * (int)threadIdx.x; n < W; n += 4 * (int)blockDim.x) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(p + n), g1 = *reinterpret_cast<const f32x4*>(p + 2 * plane + n);
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(p + plane + n), u1 = *reinterpret_cast<const f32x4*>(p + 3 * plane + n);
+      uint32_t hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_mul((g0[i] + g1[i]) * sc, (u0[i] + u1[i]) * sc));
+      *reinterpret_cast<u32x2*>(o + n) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+    }
+  }
+}
+
 size_t mfma_split_workspace_bytes(int n_w, int bits, int64_t n_rows, int N, int K) {
-  if (n_w != 1 || bits != 4 || K < 4096 || n_rows <= 0) return 0;
-  return (size_t)n_rows * (size_t)N * sizeof(float);
+  if (bits != 4 || n_rows <= 0) return 0;
+  if (n_w == 1) return K >= 4096 ? (size_t)n_rows * (size_t)N * sizeof(float) : 0;
+  // the gate/up pair: four planes of at most 16 column tiles (128 columns each), for calls
+  // of 512 to 4096 rows (fewer rows fill too few row tiles to gain from the split)
+  if (K < 2048 || n_rows < 512 || n_rows > 4096) return 0;
+  return 4 * (size_t)n_rows * (size_t)std::min(N, 16 * 128) * sizeof(float);
 }
 
 template <int BITS, int ABITS, bool LT, bool BLK>
@@ -553,9 +670,39 @@ static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream)
   const int64_t mtiles = (slots + 8 * G - 1) / (8 * G) * (8 * G);   // whole runs on every XCD
   auto grid_for = [&](int ncol) { return dim3((unsigned)((a.N + ncol - 1) / ncol), (unsigned)mtiles); };
   if (a.n_w == 2) {
-    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK, 2>), grid_for(128), dim3(256), 0, stream,
+    // 256-row tiles (4-bit codebooks) run one workgroup per CU.  In calls of few M-tiles
+    // each XCD works through its tile's column tiles in rounds of its CUs; when the last
+    // round would be at most half full, the column tiles in it split K in two with the
+    // workspace, so both halves fill that round, and a second pass forms their h.
+    int tc0 = -1, extra = 0;
+    if constexpr (BM == 256) {
+      int cus = 0;
+      if (a.ws != nullptr && mfma_split_workspace_bytes(2, BITS, a.n_rows, a.N, a.K) > 0 && mt <= 16 &&
+          device_cu_count(&cus) == hipSuccess) {
+        const int per = cus / 8;                     // CUs per XCD
+        const int ntc = (a.N + 127) / 128;
+        const int tl = per > 0 ? ntc % per : 0;      // column tiles of the last round
+        const size_t need = 16 * (size_t)a.n_rows * (size_t)(a.N - (ntc - tl) * 128);
+        if (tl > 0 && 2 * tl <= per && need <= mfma_split_workspace_bytes(2, BITS, a.n_rows, a.N, a.K) &&
+            a.ws_bytes >= need) {
+          tc0 = ntc - tl;
+          extra = tl;
+        }
+      }
+    }
+    dim3 grid = grid_for(128);
+    grid.x += (unsigned)extra;                       // the split column tiles' second halves
+    hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 2, LT, BLK, 2>), grid, dim3(256), 0, stream,
                        a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                       min_rows, a.blocked, a.out, a.ldo, nullptr);
+                       min_rows, a.blocked, a.out, a.ldo, static_cast<float*>(a.ws), tc0);
+    if (extra > 0) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const unsigned blocks = (unsigned)(a.n_rows < 4096 ? a.n_rows : 4096);
+      hipLaunchKernelGGL(mfma_swiglu_reduce_kernel, dim3(blocks), dim3(256), 0, stream,
+                         static_cast<uint16_t*>(a.out), a.ldo, static_cast<const float*>(a.ws), a.n_rows,
+                         a.N, tc0 * 128, a.scales, a.row_token, a.offsets, E, min_rows, BM);
+    }
     return hipGetLastError();
   }
   if constexpr (BM == 256) {
@@ -571,7 +718,7 @@ static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream)
       grid.z = (unsigned)nsplit;
       hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 1>), grid, dim3(256), 0, stream,
                          a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                         min_rows, a.blocked, a.out, a.ldo, static_cast<float*>(a.ws));
+                         min_rows, a.blocked, a.out, a.ldo, static_cast<float*>(a.ws), -1);
       if (nsplit > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -585,7 +732,7 @@ static hipError_t launch_p2(const GemmArgs& a, int min_rows, hipStream_t stream)
   }
   hipLaunchKernelGGL((mfma_prefill_kernel<BITS, ABITS, 1, LT, BLK, 2>), grid_for(256), dim3(256), 0, stream,
                      a.codes, a.scales, a.offsets, a.row_token, a.w[0], a.w[1], a.n_rows, E, a.N, a.K,
-                     min_rows, a.blocked, a.out, a.ldo, nullptr);
+                     min_rows, a.blocked, a.out, a.ldo, nullptr, -1);
   return hipGetLastError();
 }
 

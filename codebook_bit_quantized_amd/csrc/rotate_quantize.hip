@@ -523,7 +523,7 @@ rotate_quantize_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64
 }
 
 // Compute units of the current device, looked up once per device.
-static hipError_t device_cu_count(int* out) {
+hipError_t device_cu_count(int* out) {
   static std::atomic<int> cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

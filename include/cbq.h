@@ -297,14 +297,19 @@ int cbq_moe_route_gather_noalloc(const float* logits, int64_t T, int32_t E, int3
  *                    step at most.
  *  out, ldo        : fp32 or bf16 [R][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
  *  ws, ws_bytes    : optional device workspace (16-byte aligned; NULL / 0: none).  The GEMM
- *                    needs none.  Given at least cbq_gemm_workspace(...) bytes (nonzero only
- *                    for one weight set of 4-bit codebooks with K >= 4096 on the MFMA or
- *                    AUTO path: n_rows * N * 4), an MFMA call whose 256-row tiles would
- *                    leave CUs idle splits K in two, keeps the second half's partial sums
- *                    there and adds them to out in a second pass, in a fixed order (so the
- *                    result is deterministic and differs from the unsplit call only in the
- *                    fp32 summation order).  The workspace is scratch: its contents after
- *                    the call are unspecified, and calls that share one must not overlap.
+ *                    needs none.  cbq_gemm_workspace(...) is nonzero only for 4-bit
+ *                    codebooks on the MFMA or AUTO path: one weight set with K >= 4096
+ *                    (n_rows * N * 4 bytes), or the gate/up pair with K >= 2048 and
+ *                    512 <= n_rows <= 4096 (16 * n_rows * min(N, 2048) bytes).  Given that many
+ *                    bytes, an MFMA call whose 256-row tiles would leave CUs idle splits K
+ *                    in two: a single matrix keeps the second half's partial sums there
+ *                    and adds them to out in a second pass; the pair (in calls of at most
+ *                    8 row tiles) splits the column tiles of its last, at most half-full
+ *                    round of workgroups, keeps both halves' sums of g and u there, and a
+ *                    second pass forms their h.  The order is fixed, so the result is
+ *                    deterministic and differs from the unsplit call only in the fp32
+ *                    summation order.  The workspace is scratch: its contents after the
+ *                    call are unspecified, and calls that share one must not overlap.
  *  Rows of experts with no rows, and rows outside every expert range, are not written.
  *  Limits (CBQ_EUNSUPPORTED beyond them): the output is smaller than 1 GiB, one
  *  expert's index block and the codes array are smaller than 2 GiB each (the codes

@@ -184,8 +184,20 @@ def test_gemm_validation():
     assert lib.cbq_gemm_workspace(ctypes.pointer(w4k), 1, 16, 4, cbq.PATH_LUT) == 0
     assert lib.cbq_gemm_workspace(ctypes.pointer(w4k), 1, 16, 4, cbq.PATH_PAGES_PRODUCTS) == 0
     assert lib.cbq_gemm_workspace(ctypes.pointer(_w(K=4096, bits=3)), 1, 16, 4, cbq.PATH_AUTO) == 0
+    # the gate/up pair with 4-bit codebooks, K >= 2048 and 512 to 4096 rows: four fp32
+    # planes of the at most 16 split column tiles (2048 columns)
     pair = (cbq.cbq_weights * 2)(w4k, w4k)
-    assert lib.cbq_gemm_workspace(pair, 2, 16, 4, cbq.PATH_AUTO) == 0     # SwiGLU pair: never split
+    assert lib.cbq_gemm_workspace(pair, 2, 512, 4, cbq.PATH_AUTO) == 4 * 512 * 64 * 4
+    assert lib.cbq_gemm_workspace(pair, 2, 4096, 4, cbq.PATH_MFMA) == 4 * 4096 * 64 * 4
+    assert lib.cbq_gemm_workspace(pair, 2, 511, 4, cbq.PATH_AUTO) == 0
+    assert lib.cbq_gemm_workspace(pair, 2, 600, 8, cbq.PATH_LUT) == 0
+    assert lib.cbq_gemm_workspace(pair, 2, 4097, 8, cbq.PATH_MFMA) == 0
+    wide = _w(K=2048, N=6144)
+    assert lib.cbq_gemm_workspace((cbq.cbq_weights * 2)(wide, wide), 2, 1000, 8, cbq.PATH_MFMA) == 4 * 1000 * 2048 * 4
+    short = _w(K=1984)
+    assert lib.cbq_gemm_workspace((cbq.cbq_weights * 2)(short, short), 2, 600, 4, cbq.PATH_AUTO) == 0
+    three = _w(K=4096, bits=3)
+    assert lib.cbq_gemm_workspace((cbq.cbq_weights * 2)(three, three), 2, 600, 4, cbq.PATH_AUTO) == 0
     arr = (cbq.cbq_weights * 1)(w4k)
     assert lib.cbq_codebook_lut_gemm(ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000), 4, 16, None, None,
                                      arr, 1, 0, 0, ctypes.c_void_p(0x3000), 64, ctypes.c_void_p(0x6004),

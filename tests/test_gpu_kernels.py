@@ -449,3 +449,77 @@ def test_mfma_split_k_workspace(act_bits, K, path, dense):
                                    if 0 < counts[e] <= cbq.AUTO_MAX_LUT_ROWS])
         assert np.array_equal(s[lut_rows], p[lut_rows])
     assert not np.array_equal(s, p), "the split path ran (its sums differ in order)"
+
+
+def _bf16_steps(a, b):
+    a, b = a.astype(np.int32), b.astype(np.int32)
+    same_sign = (a ^ b) & 0x8000 == 0
+    return np.where(same_sign, np.abs(a - b), np.abs((a & 0x7FFF) + (b & 0x7FFF)))
+
+
+@pytest.mark.parametrize("case", ["auto_ragged", "mfma_many_tiles", "dense"])
+def test_mfma_gate_up_tail_split(case):
+    """The gate/up pair with 4-bit codebooks (256-row tiles, one workgroup per CU), given
+    the workspace cbq_gemm_workspace asks for: in a call of at most 8 row tiles each XCD
+    works through one tile's column tiles in rounds of its CUs, and the column tiles of a
+    last round at most half full split K in two; both halves' sums of g and u go to the
+    workspace and a second pass forms h.  h equals the oracle's within the SwiGLU
+    tolerance and the unsplit call within one bf16 step; the split call is deterministic
+    (stale workspace contents, two calls); rows AUTO sends to the LUT path are untouched.
+    With more than 8 row tiles the call does not split (bit-identical to the unsplit call).
+    N = 4672 leaves a ragged last column tile inside the split ones."""
+    K, act_bits = 2048, 8
+    if case == "dense":
+        E, N, T, path = 1, 4224, 600, cbq.PATH_MFMA
+        counts = np.array([T])
+    else:
+        E, N, T = 10, 4672, 700
+        path = cbq.PATH_AUTO if case == "auto_ragged" else cbq.PATH_MFMA
+        counts = np.array([140, 0, 17, 250, 129, 32, 200, 90, 160, 256])
+    rng = np.random.default_rng(len(case))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    dense = case == "dense"
+    row_token = None if dense else rng.integers(0, T, R).astype(np.int32)
+    rq = oracle.rotate_quantize(datagen.random_tokens(950 + len(case), T, K), 0, act_bits)
+    wn = [datagen.random_weights(960 + m, E, N, K, 4, keep_raw=False) for m in range(2)]
+    G, U = upload_weights(wn[0]), upload_weights(wn[1])
+    need = cbq.gemm_workspace([G, U], R, act_bits, path)
+    assert need == 4 * R * 2048 * 4
+    min_rows = cbq.AUTO_MAX_LUT_ROWS if path == cbq.PATH_AUTO else 0
+    tiles = int(np.sum(np.where(counts > min_rows, (counts + 255) // 256, 0)))
+    per = torch.cuda.get_device_properties(0).multi_processor_count // 8
+    ntc = (N + 127) // 128
+    splits = tiles <= 8 and 0 < ntc % per <= per // 2
+    print(f"{case}: {tiles} row tiles, {ntc} column tiles, {per} CUs per XCD, split {splits}")
+    kw = dict(expert_offsets=None if dense else to_dev(offsets),
+              row_token=None if dense else to_dev(row_token), path=path, n_rows=R)
+    args = (to_dev(rq["codes"]), to_dev(rq["scale"]), act_bits, [G, U])
+    plain = bf16_to_bits(cbq.codebook_lut_gemm(*args, **kw))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)      # stale contents
+    split = bf16_to_bits(cbq.codebook_lut_gemm(*args, ws=ws, **kw))
+    split2 = bf16_to_bits(cbq.codebook_lut_gemm(*args, ws=ws, **kw))
+    assert np.array_equal(split, split2), "the split call is deterministic"
+    ref = [oracle.expert_gemm(rq["q"], rq["scale"], row_token, None if dense else offsets,
+                              w.idx, w.codebook, K, 4) for w in wn]
+    rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in range(E)
+                           if counts[e] > min_rows])
+    want = oracle.silu_mul_bf16(ref[0], ref[1])
+    assert_bf16_close(split[rows], want[rows], f"swiglu {case}")
+    if path == cbq.PATH_AUTO:
+        lut_rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in range(E)
+                                   if 0 < counts[e] <= min_rows])
+        assert np.array_equal(split[lut_rows], plain[lut_rows])
+    # the split halves' sums land in the workspace; h left of the split column tiles is
+    # computed exactly as without it
+    used = bool((ws != 0x7F).any().item())
+    assert used == splits
+    c0 = (ntc - ntc % per) * 128 if splits else N
+    assert np.array_equal(split[:, :c0], plain[:, :c0])
+    # right of it only the fp32 order of the two halves' sums differs: an absolute change
+    # of a few units in the last place of the partial sums, which moves h by more than one
+    # bf16 step only where g or u nearly cancels (h small against the tile's values)
+    assert_bf16_close(split[rows], plain[rows], f"split vs unsplit {case}")
+    steps = _bf16_steps(split[rows], plain[rows])
+    print(f"{case}: split h equal to unsplit for {np.mean(steps == 0):.6f} of values, "
+          f"within one bf16 step for {np.mean(steps <= 1):.7f}")

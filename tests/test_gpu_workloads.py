@@ -260,6 +260,9 @@ def test_moe8_prefill_layer():
     x, lg = datagen.moe_tokens(wl, 512)
     ph, path = run_bench_phase(wl, W, x, lg, decode=False)
     assert path == cbq.PATH_MFMA
+    # the benchmark's gate/up call carries the workspace of its tail K split, and the down
+    # call that of its K split
+    assert ph.ws_gu is not None and ph.ws_dn is not None
     check_moe_phase(wl, host, ph, x, lg, seed=300, extra_paths=(cbq.PATH_LUT,))
 
 
