@@ -293,8 +293,10 @@ int cbq_moe_route_gather_noalloc(const float* logits, int64_t T, int32_t E, int3
  *                    The SwiGLU epilogue is one fp32 formula on every path
  *                    (g * u * rcp(1 + exp(-g)) with the hardware exp2 and reciprocal),
  *                    so the bf16 h of two paths differs only where that summation
- *                    order moves g or u across a bf16 rounding boundary: by one bf16
- *                    step at most.
+ *                    order moves g or u across a bf16 rounding boundary: mostly by one
+ *                    bf16 step, by more only where g or u nearly cancels (the fp32
+ *                    order changes them by units in the last place of their partial
+ *                    sums, large against a small h).
  *  out, ldo        : fp32 or bf16 [R][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
  *  ws, ws_bytes    : optional device workspace (16-byte aligned; NULL / 0: none).  The GEMM
  *                    needs none.  cbq_gemm_workspace(...) is nonzero only for 4-bit

@@ -463,8 +463,9 @@ def test_mfma_gate_up_tail_split(case):
     the workspace cbq_gemm_workspace asks for: in a call of at most 8 row tiles each XCD
     works through one tile's column tiles in rounds of its CUs, and the column tiles of a
     last round at most half full split K in two; both halves' sums of g and u go to the
-    workspace and a second pass forms h.  h equals the oracle's within the SwiGLU
-    tolerance and the unsplit call within one bf16 step; the split call is deterministic
+    workspace and a second pass forms h.  h equals the oracle's, and the unsplit call's,
+    within the SwiGLU tolerance (bit for bit left of the split columns); the split call is
+    deterministic
     (stale workspace contents, two calls); rows AUTO sends to the LUT path are untouched.
     With more than 8 row tiles the call does not split (bit-identical to the unsplit call).
     N = 4672 leaves a ragged last column tile inside the split ones."""
