@@ -279,7 +279,8 @@ def prepack_weights(w: CodebookWeights, stream=None) -> CodebookWeights:
 def gemm_workspace(weights: Sequence[CodebookWeights], n_rows: int, act_bits: int,
                    path: int = PATH_AUTO) -> int:
     """Bytes of optional GEMM workspace (cbq_gemm_workspace): with it, a single-matrix MFMA
-    call whose tiles would leave CUs idle splits K in two; 0 when no call of these sizes can."""
+    call whose tiles would leave CUs idle splits K in two, and a 4-bit gate/up call the
+    column tiles of a half-empty last round; 0 when no call of these sizes can."""
     arr = (cbq_weights * len(weights))(*[w.c_struct() for w in weights])
     return int(load_library().cbq_gemm_workspace(arr, len(weights), n_rows, act_bits, path))
 
@@ -392,14 +393,22 @@ def moe_ffn(x: torch.Tensor, logits: torch.Tensor, gate: CodebookWeights, up: Co
     """One MoE FFN layer as a sequence of the four library calls (no compute here).
 
     gate/up/down hold E routed + n_shared shared experts.  Returns y fp32 [T][H], or
-    (y, intermediates) when keep is True."""
+    (y, intermediates) when keep is True.  The GEMMs get the optional workspaces
+    gemm_workspace asks for."""
     codes, scales = rotate_quantize(x, act_bits, stream=stream)
     rt = moe_route_gather(logits, topk, renormalize, n_shared, stream=stream)
+    R = int(rt["sorted_tokens"].shape[0])
+
+    def workspace(ws):
+        n = gemm_workspace(ws, R, act_bits, path)
+        return torch.empty((n,), dtype=torch.uint8, device=x.device) if n > 0 else None
+
     h = codebook_lut_gemm(codes, scales, act_bits, [gate, up], expert_offsets=rt["offsets"],
-                          row_token=rt["sorted_tokens"], path=path, stream=stream)
+                          row_token=rt["sorted_tokens"], path=path, ws=workspace([gate, up]),
+                          stream=stream)
     codes_h, scales_h = rotate_quantize(h, act_bits, stream=stream)
     out = codebook_lut_gemm(codes_h, scales_h, act_bits, [down], expert_offsets=rt["offsets"],
-                            path=path, stream=stream)
+                            path=path, ws=workspace([down]), stream=stream)
     y = moe_combine(out, rt["slot_of"], rt["weights"], n_shared, stream=stream)
     if keep:
         return y, dict(codes=codes, scales=scales, route=rt, h=h, codes_h=codes_h,

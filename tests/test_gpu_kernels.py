@@ -524,3 +524,37 @@ def test_mfma_gate_up_tail_split(case):
     steps = _bf16_steps(split[rows], plain[rows])
     print(f"{case}: split h equal to unsplit for {np.mean(steps == 0):.6f} of values, "
           f"within one bf16 step for {np.mean(steps <= 1):.7f}")
+
+
+def test_moe_ffn_with_workspaces():
+    """moe_ffn hands its GEMMs the workspaces gemm_workspace asks for.  At 300 tokens, top-2
+    of 4 routed experts (600 rows of 137-161 each, 4-bit codebooks, H 2048, F 4224, A8) both
+    K splits run: the gate/up pair's last column tile on each XCD, and the down projection
+    (K = 4224).  Every stage against the oracle, teacher forced on the GPU's own
+    intermediates."""
+    T, E, k, S, H, F, a = 300, 4, 2, 0, 2048, 4224, 8
+    wl, gate, up, down, x, lg = _moe_case(77, T, E, k, S, H, F, 4, a)
+    G, U, D = upload_weights(gate), upload_weights(up), upload_weights(down)
+    R = T * k
+    assert cbq.gemm_workspace([G, U], R, a) > 0 and cbq.gemm_workspace([D], R, a) > 0
+    y, mid = cbq.moe_ffn(bf16_dev(x), to_dev(lg), G, U, D, k, S, a, keep=True)
+    torch.cuda.synchronize()
+    rq = oracle.rotate_quantize(x, 0, a)
+    assert rq["ok"].all()
+    assert np.array_equal(mid["codes"].cpu().numpy(), rq["codes"])
+    rt = oracle.route(lg, k, True, S)
+    for key in ("offsets", "sorted_tokens", "slot_of"):
+        assert np.array_equal(mid["route"][key].cpu().numpy(), rt[key]), key
+    g = oracle.expert_gemm(rq["q"], rq["scale"], rt["sorted_tokens"], rt["offsets"], gate.idx,
+                           gate.codebook, H, 4)
+    u = oracle.expert_gemm(rq["q"], rq["scale"], rt["sorted_tokens"], rt["offsets"], up.idx,
+                           up.codebook, H, 4)
+    h = bf16_to_bits(mid["h"])
+    assert_bf16_close(h, oracle.silu_mul_bf16(g, u), "h")
+    rqh = oracle.rotate_quantize(h, 0, a)
+    assert np.array_equal(mid["codes_h"].cpu().numpy(), rqh["codes"])
+    d = oracle.expert_gemm(rqh["q"], rqh["scale"], None, rt["offsets"], down.idx, down.codebook, F, 4)
+    out = mid["out"].cpu().numpy()
+    assert_normwise(out, d, 1e-3, "down")
+    y_ref = oracle.combine(out, rt["slot_of"], rt["weights"], T, k, S)
+    assert_normwise(y.cpu().numpy(), y_ref, 1e-3, "y")
